@@ -1,0 +1,40 @@
+"""Bit-exact reference for the KV write path and copy-on-write block copies.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+[IV §PagedAttention: What the OS Figured Out Decades Ago]: as tokens are
+generated their keys/values are appended, and new blocks are added to the
+sequence's block table.  Each new token therefore goes to one *slot*:
+``slot = physical_block * B + offset``.  A negative slot means "no write"
+(padding tokens).
+
+[IV §Copy-on-Write Makes Beam Search Cheap], [RW §How PagedAttention Works]:
+when a branch writes into a shared block, that block is copied first; the copy
+is a whole-block duplicate of K and V for every KV head.
+
+Operates in place on raw 16-bit patterns (numpy uint16 or float16), so the
+result is compared bit for bit.  Storage format:
+k_cache [N, Hkv, B, D] (slot-major), v_cache [N, Hkv, D, B] (dim-major).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
+             v: np.ndarray, slot_mapping, block_size: int) -> None:
+    """For each token i with slot_mapping[i] >= 0 store k[i], v[i] (each
+    [Hkv, D]) into the slot; tokens are applied in index order."""
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        blk, off = divmod(int(slot), block_size)
+        k_cache[blk, :, off, :] = k[i]
+        v_cache[blk, :, :, off] = v[i]
+
+
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> None:
+    """Apply (src, dst) whole-block copies in order, K and V, all heads."""
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        k_cache[dst] = k_cache[src]
+        v_cache[dst] = v_cache[src]

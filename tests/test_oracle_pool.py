@@ -1,0 +1,243 @@
+"""Pins for the pool model, the write-path reference, SplitMix64 and the
+KV-size closed form.
+
+What fixes each expectation:
+  * SplitMix64: the published reference implementation's output for seed
+    1234567 and for seed 0 (widely reproduced test vectors).
+  * KV size: the worked values printed on the pages (tests/golden/).
+  * pool: invariants the pages state (blocks claimed on demand and released
+    at once when a sequence ends; shared blocks copied only when a branch
+    writes into them; only the last block of a sequence is partly empty;
+    concurrency ceiling = blocks in the pool / blocks per sequence), plus a
+    hand-traced copy-on-write scenario.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+from oracle import kv_cache as KC
+from oracle import kv_size as KS
+from oracle.pool_model import PoolError, PoolModel
+from oracle.splitmix64 import SplitMix64, shuffled_order
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# SplitMix64 test vectors
+# ---------------------------------------------------------------------------
+
+def test_splitmix64_reference_vectors():
+    g = SplitMix64(1234567)
+    assert [g.next() for _ in range(5)] == [
+        6457827717110365317, 3203168211198807973, 9817491932198370423,
+        4593380528125082431, 16408922859458223821]
+    assert SplitMix64(0).next() == 0xE220A8397B1DCDAF
+
+
+def test_shuffle_is_a_permutation_and_seed_zero_is_identity():
+    for n, seed in [(1, 5), (2, 9), (64, 4221), (1000, 7)]:
+        o = shuffled_order(n, seed)
+        assert sorted(o) == list(range(n))
+    assert shuffled_order(50, 0) == list(range(50))
+    assert shuffled_order(50, 3) != list(range(50))
+
+
+# ---------------------------------------------------------------------------
+# closed form (pages' worked values)
+# ---------------------------------------------------------------------------
+
+def test_kv_size_matches_pages_worked_values():
+    with open(os.path.join(GOLDEN, "kv_size_worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = KS.kv_bytes(c["num_layers"], c["seq_len"], c["hidden"], c["dtype_bytes"]) / 1e9
+        if "accept_rel" in c:
+            assert abs(got - c["pages_value_gb"]) <= c["accept_rel"] * c["pages_value_gb"], c
+        else:
+            assert abs(got - c["pages_value_gb"]) <= c["accept_abs_gb"], c
+    # the exact value behind both statements
+    assert KS.kv_bytes(40, 2048, 5120, 2) == 1_677_721_600
+
+
+def test_gqa_form_reduces_to_hidden_form_for_mha():
+    assert KS.kv_bytes_gqa(32, 1000, 32, 128, 2) == KS.kv_bytes(32, 1000, 4096, 2)
+    # 8 KV heads hold a quarter of the MHA bytes
+    assert KS.kv_bytes_gqa(32, 1000, 8, 128, 2) * 4 == KS.kv_bytes(32, 1000, 4096, 2)
+
+
+def test_paged_waste_below_pages_bound_on_synthetic_lengths():
+    """Under paging only each sequence's last block is partly empty; the
+    pages quote under 4% waste versus 60-80% for max-length reservation."""
+    rng = np.random.default_rng(4222)
+    lens = rng.integers(128, 2049, size=64)
+    w_paged = KS.paged_waste_fraction(lens, 16)
+    w_res = KS.reserved_waste_fraction(lens, 2048)
+    assert w_paged < 0.04
+    assert w_res > 0.4
+    held = [-(-L // 16) * 16 for L in lens]
+    assert all(0 <= h - L < 16 for h, L in zip(held, lens))
+    assert KS.paged_bytes(1, 17, 8, 2, 16) == KS.kv_bytes(1, 32, 8, 2)
+
+
+# ---------------------------------------------------------------------------
+# write path reference
+# ---------------------------------------------------------------------------
+
+def test_write_kv_places_tokens_and_skips_negative_slots():
+    N, H, B, D = 6, 2, 16, 4
+    kc = np.full((N, H, B, D), 0xFFFF, np.uint16)
+    vc = np.full((N, H, D, B), 0xFFFF, np.uint16)
+    k = np.arange(3 * H * D, dtype=np.uint16).reshape(3, H, D)
+    v = (1000 + np.arange(3 * H * D)).astype(np.uint16).reshape(3, H, D)
+    KC.write_kv(kc, vc, k, v, [5 * 16 + 15, -1, 2 * 16 + 0], 16)
+    assert np.array_equal(kc[5, :, 15, :], k[0]) and np.array_equal(vc[5, :, :, 15], v[0])
+    assert np.array_equal(kc[2, :, 0, :], k[2]) and np.array_equal(vc[2, :, :, 0], v[2])
+    touched = np.zeros((N, B), bool); touched[5, 15] = touched[2, 0] = True
+    for b in range(N):
+        for o in range(B):
+            if not touched[b, o]:
+                assert np.all(kc[b, :, o, :] == 0xFFFF) and np.all(vc[b, :, :, o] == 0xFFFF)
+
+
+def test_copy_blocks_copies_whole_blocks_in_order():
+    rng = np.random.default_rng(1)
+    kc = rng.integers(0, 65535, (5, 2, 16, 4)).astype(np.uint16)
+    vc = rng.integers(0, 65535, (5, 2, 4, 16)).astype(np.uint16)
+    k0, v0 = kc.copy(), vc.copy()
+    KC.copy_blocks(kc, vc, [(1, 3), (3, 4)])
+    assert np.array_equal(kc[3], k0[1]) and np.array_equal(kc[4], k0[1])
+    assert np.array_equal(vc[4], v0[1]) and np.array_equal(kc[0], k0[0])
+
+
+# ---------------------------------------------------------------------------
+# pool model
+# ---------------------------------------------------------------------------
+
+def check_invariants(p: PoolModel):
+    live = {}
+    for sid, t in p.tables.items():
+        n = p.ntok[sid]
+        assert len(t) == -(-n // p.B)                     # only the last block is partial
+        for b in t:
+            live[b] = live.get(b, 0) + 1
+    for b in range(p.N):
+        assert p.refcount(b) == live.get(b, 0)
+    assert p.num_free() + len(live) == p.N
+    assert len(set(p.stack)) == len(p.stack)
+    assert not (set(p.stack) & set(live))
+
+
+def test_hand_traced_copy_on_write():
+    """Beam-style branching: a 20-token prompt (one full block + 4 tokens)
+    forked 3 times.  The full block stays shared; the first write of each
+    branch into the partial block copies exactly that block."""
+    p = PoolModel(16, 16, seed=0)           # identity order: blocks 0, 1, 2, ...
+    a = p.seq_create()
+    slots, cow = p.seq_append(a, 20)
+    assert slots == list(range(0, 20)) and cow == []
+    kids = [p.seq_fork(a) for _ in range(3)]
+    assert p.refcount(0) == 4 and p.refcount(1) == 4
+    s1, c1 = p.seq_append(kids[0], 1)
+    assert c1 == [(1, 2)] and s1 == [2 * 16 + 4]
+    assert p.refcount(1) == 3 and p.refcount(2) == 1 and p.refcount(0) == 4
+    s2, c2 = p.seq_append(kids[0], 1)          # now private: no copy
+    assert c2 == [] and s2 == [2 * 16 + 5]
+    for k in kids[1:]:
+        _, c = p.seq_append(k, 1)
+        assert len(c) == 1 and c[0][0] == 1
+    assert p.refcount(1) == 1                  # only the parent still holds it
+    s, c = p.seq_append(a, 1)                  # the last holder writes in place
+    assert c == [] and s == [1 * 16 + 4]
+    check_invariants(p)
+    for sid in [a] + kids:
+        p.seq_free(sid)
+    assert p.num_free() == 16
+
+
+def test_full_shared_block_is_not_copied():
+    p = PoolModel(8, 16, seed=0)
+    a = p.seq_create()
+    p.seq_append(a, 32)
+    b = p.seq_fork(a)
+    slots, cow = p.seq_append(b, 1)
+    assert cow == [] and slots == [2 * 16]
+    assert p.refcount(0) == 2 and p.refcount(1) == 2 and p.refcount(2) == 1
+
+
+def test_enomem_is_all_or_nothing():
+    p = PoolModel(4, 16, seed=3)
+    a = p.seq_create()
+    p.seq_append(a, 50)                         # 4 blocks
+    before = (list(p.stack), list(p.ref), {k: list(v) for k, v in p.tables.items()}, dict(p.ntok))
+    b = p.seq_fork(a)
+    with pytest.raises(PoolError) as e:
+        p.seq_append(b, 1)                      # needs one CoW block: none free
+    assert e.value.code == "ENOMEM"
+    assert p.tables[b] == before[2][a] and p.ntok[b] == 50
+    assert list(p.stack) == before[0]
+    with pytest.raises(PoolError):
+        p.seq_free(999)
+
+
+def test_free_returns_blocks_lifo_and_reuses_them_first():
+    p = PoolModel(10, 16, seed=77)
+    order = shuffled_order(10, 77)
+    a = p.seq_create()
+    p.seq_append(a, 40)                         # 3 blocks
+    assert p.tables[a] == order[:3]
+    p.seq_free(a)
+    assert p.num_free() == 10
+    b = p.seq_create()
+    p.seq_append(b, 16)
+    assert p.tables[b] == [order[2]]            # the last freed block is on top
+
+
+def test_concurrency_ceiling():
+    """Blocks in the pool divided by blocks per sequence bounds how many
+    sequences fit (Inside vLLM, section 'Tuning in Practice')."""
+    N, L = 100, 200                             # 13 blocks per sequence
+    p = PoolModel(N, 16, seed=5)
+    fitted = 0
+    while True:
+        s = p.seq_create()
+        try:
+            p.seq_append(s, L)
+        except PoolError:
+            break
+        fitted += 1
+    assert fitted == N // (-(-L // 16))
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.integers(0, 3), st.integers(0, 40), st.integers(0, 7)),
+                min_size=1, max_size=60),
+       st.integers(0, 2 ** 32))
+def test_random_operations_keep_invariants(ops, seed):
+    p = PoolModel(24, 16, seed=seed)
+    seqs = []
+    for op, n, pick in ops:
+        try:
+            if op == 0 or not seqs:
+                seqs.append(p.seq_create())
+            elif op == 1:
+                seqs.append(p.seq_fork(seqs[pick % len(seqs)]))
+            elif op == 2:
+                sid = seqs[pick % len(seqs)]
+                before_last = p.tables[sid][-1] if p.tables[sid] else None
+                partial = p.ntok[sid] % 16 != 0
+                shared = before_last is not None and p.refcount(before_last) > 1
+                _, cow = p.seq_append(sid, n)
+                assert (len(cow) == 1) == (n > 0 and partial and shared)
+            else:
+                p.seq_free(seqs.pop(pick % len(seqs)))
+        except PoolError as e:
+            assert e.code == "ENOMEM"
+        check_invariants(p)
+    for s in seqs:
+        p.seq_free(s)
+    assert p.num_free() == 24
