@@ -1,0 +1,216 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache attention for AMD MI355X (gfx950).
+ *
+ * The method (PagedAttention) keeps each sequence's keys and values in
+ * fixed-size blocks (16 tokens by default) scattered through one pool, and
+ * reaches them through a per-sequence block table; attention reads the blocks
+ * as if they were one contiguous sequence ("Inside vLLM: How PagedAttention
+ * Changes Python LLM Inference at the Systems Level", section "PagedAttention:
+ * What the OS Figured Out Decades Ago"; "vLLM PagedAttention: Reducing KV
+ * Cache Memory Waste", section "How PagedAttention Works").  Sequences that
+ * branch from one prompt share its blocks by reference count; a shared block
+ * is copied only when a branch writes into it ("Inside vLLM ...", section
+ * "Copy-on-Write Makes Beam Search Cheap").
+ *
+ * Conventions for every call
+ *   - Every call returns pa_status; nothing throws or aborts across the ABI.
+ *     On failure pa_last_error() describes the cause (thread-local string,
+ *     valid until this thread's next pa_* call).
+ *   - Device calls take DEVICE pointers owned by the caller, enqueue their
+ *     kernels on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and return after the launch without synchronising.  Arguments
+ *     are checked on the host before anything is launched; a rejected call
+ *     launches nothing.
+ *   - The library never allocates device memory.
+ *   - dtype: K, V, Q and outputs share one 16-bit storage type; arithmetic is
+ *     fp32 (MFMA fp32 accumulate); outputs are rounded to nearest even.
+ *   - Supported: head_dim 64 or 128, block_size 16, fp16 or bf16,
+ *     num_q_heads a multiple of num_kv_heads.  Anything else: PA_ENOTSUP.
+ *   - Pointers to 16-bit data must be 16-byte aligned.
+ *
+ * KV cache storage (one pair of tensors per layer, caller-allocated):
+ *   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]   slot-major
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
+ * Token t of a sequence lives in block block_table[t / block_size], slot
+ * t % block_size; its storage address ("slot") is block * block_size + slot.
+ * One (block, kv head) tile is contiguous in both tensors (4 KiB at D = 128).
+ * V is stored dim-major so that the attention kernels can feed it straight
+ * into the matrix cores, whose operands run along the key index for P.V.
+ *
+ * Device data (block ids, slots, context lengths) is checked inside the
+ * kernels: an out-of-range slot or pair is skipped by the write and copy
+ * kernels, and a sequence with an out-of-range block id or context length
+ * gets NaN output rows.  No call reads or writes outside the buffers it is
+ * given when the sizes passed to it are right.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,   /* bad argument (null pointer, negative size, bad id)   */
+  PA_ENOMEM = 2,   /* block pool exhausted (pool calls only)                */
+  PA_EHIP = 3,     /* a HIP runtime call or kernel launch failed            */
+  PA_ENOTSUP = 4   /* valid but unsupported shape / dtype / alignment      */
+} pa_status;
+
+typedef enum { PA_FP16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* pa_last_error(void);
+/* Library version string, e.g. "libpa 0.1 gfx950". */
+const char* pa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Slot-mapped KV write.  New tokens' keys and values are appended to their
+ * sequence's blocks as they are generated ("Inside vLLM ...", section
+ * "PagedAttention: What the OS Figured Out Decades Ago").
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim], token i starting at
+ *                 element i * src_token_stride (heads contiguous after it);
+ *                 src_token_stride >= num_kv_heads*head_dim, multiple of 8.
+ *   k_cache, v_cache   the caches above, num_blocks blocks each.
+ *   slot_mapping  [num_tokens] int64, device: storage slot of token i, or a
+ *                 negative value to skip the token.  Slots must be distinct
+ *                 (two tokens writing one slot race).
+ * Bit-exact copy: the cache holds exactly the bits of k and v afterwards.
+ * num_tokens == 0 launches nothing and returns PA_OK.
+ * ---------------------------------------------------------------------- */
+pa_status pa_write_kv(const void* k, const void* v, int64_t src_token_stride,
+                      void* k_cache, void* v_cache, int64_t num_blocks,
+                      const int64_t* slot_mapping, int32_t num_tokens,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Whole-block copies for copy-on-write ("Inside vLLM ...", section
+ * "Copy-on-Write Makes Beam Search Cheap").
+ *   pairs   [num_pairs][2] int32, device: (src, dst) physical block ids.
+ * Copies K and V of every KV head of src to dst, bit-exact.  Pairs run
+ * concurrently: a dst must not be the src or dst of another pair.
+ * ---------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
+                         const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention: one query token per sequence attends to all
+ * context_lens[s] keys of its sequence (the newest token's K/V must already be
+ * written).  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ *   out, q          [num_seqs][num_q_heads][head_dim], contiguous.
+ *   block_tables    [num_seqs][bt_stride] int32, device.
+ *   context_lens    [num_seqs] int32, device; 0 gives a zero row; a length
+ *                   above max_context_len or bt_stride*block_size gives NaN.
+ *   max_context_len host-side upper bound of context_lens (sizes the grid).
+ *   scale           softmax scale (usually 1/sqrt(head_dim)).
+ *   partition_size  long contexts are cut into partitions of this many
+ *                   tokens, each handled by its own workgroup, and merged by
+ *                   log-sum-exp in a second kernel.  0 = library default
+ *                   (pa_default_partition_size).  Multiple of 16, <= 1024.
+ *                   The result for a sequence depends only on its own data
+ *                   and on the partition size, never on the rest of the batch.
+ *   workspace       device scratch of at least pa_decode_workspace_size()
+ *                   bytes for the same arguments (may be NULL if that size is
+ *                   0); contents need not be initialised.
+ * ---------------------------------------------------------------------- */
+int32_t   pa_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim);
+pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_size,
+                                   int32_t num_kv_heads, size_t* bytes);
+pa_status pa_decode(void* out, const void* q,
+                    const void* k_cache, const void* v_cache, int64_t num_blocks,
+                    const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_context_len, float scale,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Chunked prefill: the scheduler serves decode first and fills the rest of
+ * the step's token budget with prefill chunks ("PagedAttention in vLLM: A
+ * Throughput Settings Guide", section "Tuning Batching, Prefill, and Cache").
+ * Chunk c continues its own sequence: its n_c query rows are the sequence's
+ * newest tokens, already written to the cache, so row j (0-based) sits at
+ * position seq_lens[c] - n_c + j and attends keys 0 .. seq_lens[c] - n_c + j.
+ *
+ *   out, q        [total_rows][num_q_heads][head_dim] packed; chunk c owns
+ *                 rows q_start_loc[c] .. q_start_loc[c+1]-1.
+ *   q_start_loc   [num_chunks+1] int32, device, non-decreasing, from 0.
+ *   seq_lens      [num_chunks] int32, device: keys of chunk c's sequence
+ *                 after the chunk, >= n_c.
+ *   block_tables  [num_chunks][bt_stride] int32, device.
+ *   max_q_len     host bound on n_c (sizes the grid).
+ *   max_seq_len   host bound on seq_lens (a longer sequence gets NaN rows).
+ * ---------------------------------------------------------------------- */
+pa_status pa_prefill_chunk(void* out, const void* q,
+                           const void* k_cache, const void* v_cache, int64_t num_blocks,
+                           const int32_t* block_tables, int32_t bt_stride,
+                           const int32_t* q_start_loc, const int32_t* seq_lens,
+                           int32_t num_chunks, int32_t max_q_len, int32_t max_seq_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, float scale, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host-side block pool: refcounted blocks, per-sequence block tables and
+ * copy-on-write ("Inside vLLM ...", sections "PagedAttention: What the OS
+ * Figured Out Decades Ago", "Copy-on-Write Makes Beam Search Cheap" and
+ * "Python LLM Inference Optimization with vLLM: Parameters That Actually
+ * Matter", where the allocator is the pool's page-frame table).
+ * The pool is library-owned, not thread-safe (one owner thread), and holds
+ * only ids: the caller moves the data with pa_copy_blocks / pa_write_kv.
+ *
+ * Allocation order: the free list is a LIFO stack whose initial order is a
+ * Fisher-Yates shuffle of [0, num_blocks) driven by SplitMix64(seed)
+ * (seed 0: identity order); the first block handed out is order[0]; a freed
+ * block goes on top and is handed out next.  Sequence ids count up from 1.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_pool pa_pool;
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed,
+                         pa_pool** out);
+void      pa_pool_destroy(pa_pool* pool);                 /* NULL-safe */
+int32_t   pa_pool_num_free(const pa_pool* pool);          /* -1 if pool is NULL */
+int32_t   pa_pool_num_blocks(const pa_pool* pool);        /* -1 if pool is NULL */
+int32_t   pa_block_refcount(const pa_pool* pool, int32_t block); /* -1 if out of range */
+
+/* New empty sequence (0 tokens, 0 blocks). */
+pa_status pa_seq_create(pa_pool* pool, int64_t* seq_id);
+/* New sequence sharing every block of `parent` (each gains a reference). */
+pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t* child);
+/* Append n_tokens tokens.  Writes their storage slots to slot_mapping_out
+ * [n_tokens] (host, caller-owned).  A copy-on-write copy happens exactly when
+ * a token goes into a partly filled last block whose refcount is above one:
+ * the sequence gets a fresh block and (old, new) is written to cow_pairs_out
+ * [cow_cap][2] (host); at most one pair per call, so cow_cap >= 1 suffices.
+ * All-or-nothing: if the free blocks cannot cover the new blocks plus the
+ * copy, returns PA_ENOMEM and changes nothing. */
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens,
+                        int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                        int32_t cow_cap, int32_t* n_cow);
+/* Drop one reference from every block of seq, in table order; blocks that
+ * reach zero go back on the free stack in that order. */
+pa_status pa_seq_free(pa_pool* pool, int64_t seq);
+/* Block table of one sequence: up to cap ids into out (host). */
+pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap,
+                             int32_t* n_blocks, int32_t* n_tokens);
+/* Block tables of n sequences as rows of a [n][stride] int32 host array,
+ * unused entries set to pad; context lengths into ctx_out[n] (may be NULL).
+ * PA_EINVAL if a table is longer than stride. */
+pa_status pa_seq_block_tables(const pa_pool* pool, const int64_t* seq_ids, int32_t n,
+                              int32_t* out, int32_t stride, int32_t pad, int32_t* ctx_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

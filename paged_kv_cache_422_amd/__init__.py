@@ -1,0 +1,246 @@
+"""Thin Python binding over libpa.so (paged KV-cache attention for MI355X).
+
+Argument marshalling only: tensors become raw device pointers, the current
+torch stream becomes the hipStream_t, and every step of the hot path runs in
+the library's HIP kernels.  There is no fallback: if libpa.so is missing the
+import fails loudly (build it with ``python -m paged_kv_cache_422_amd.build``
+or ``__graft_entry__.build()``).
+
+Function names and arguments follow include/pa.h.  Cache tensors use the
+library's storage format:
+    k_cache [num_blocks, num_kv_heads, 16, head_dim]
+    v_cache [num_blocks, num_kv_heads, head_dim, 16]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# One HIP runtime per process: torch brings its own libamdhip64, and libpa
+# must bind to that same runtime (it shares torch's memory and streams), so
+# torch is loaded before libpa.so resolves its HIP dependency.
+import torch  # noqa: F401  (load order matters)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libpa.so not found at {LIB_PATH}; build it first "
+                      "(python -m paged_kv_cache_422_amd.build)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_ENOTSUP = range(5)
+PA_FP16, PA_BF16 = 0, 1
+_STATUS = {1: "EINVAL", 2: "ENOMEM", 3: "EHIP", 4: "ENOTSUP"}
+
+c_i32, c_i64, c_u64, c_f32, c_sz, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                          ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p)
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+P_i64 = ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_write_kv": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32,
+                            c_i32, c_i32, c_vp]),
+    "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_default_partition_size": (c_i32, [c_i32, c_i32, c_i32]),
+    "pa_decode_workspace_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                         ctypes.POINTER(c_sz)]),
+    "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
+                          c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_i32, c_vp]),
+    "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32,
+                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "pa_pool_create": (c_i32, [c_i32, c_i32, c_u64, ctypes.POINTER(c_vp)]),
+    "pa_pool_destroy": (None, [c_vp]),
+    "pa_pool_num_free": (c_i32, [c_vp]),
+    "pa_pool_num_blocks": (c_i32, [c_vp]),
+    "pa_block_refcount": (c_i32, [c_vp, c_i32]),
+    "pa_seq_create": (c_i32, [c_vp, P_i64]),
+    "pa_seq_fork": (c_i32, [c_vp, c_i64, P_i64]),
+    "pa_seq_append": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, c_i32, P_i32]),
+    "pa_seq_free": (c_i32, [c_vp, c_i64]),
+    "pa_seq_block_table": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32, P_i32]),
+    "pa_seq_block_tables": (c_i32, [c_vp, P_i64, c_i32, P_i32, c_i32, c_i32, P_i32]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PAError(status, _lib.pa_last_error().decode())
+
+
+def last_error() -> str:
+    return _lib.pa_last_error().decode()
+
+
+def version() -> str:
+    return _lib.pa_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors in, launches on the current stream)
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return PA_FP16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """k, v [T, Hkv, D] (token stride may exceed Hkv*D); slot_mapping int64 [T]."""
+    T, H, D = k.shape
+    assert v.shape == k.shape and v.stride() == k.stride()
+    assert k.stride(2) == 1 and k.stride(1) == D
+    _check(_lib.pa_write_kv(_ptr(k), _ptr(v), k.stride(0), _ptr(k_cache), _ptr(v_cache),
+                            k_cache.shape[0], _ptr(slot_mapping), T, H, D, k_cache.shape[2],
+                            _dtype_code(k), _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None):
+    """pairs int32 [n, 2] device tensor of (src, dst)."""
+    N, H, B, D = k_cache.shape
+    _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), N, _ptr(pairs), pairs.shape[0],
+                               H, D, B, _dtype_code(k_cache), _stream(stream)))
+
+
+def default_partition_size(num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(_lib.pa_default_partition_size(num_q_heads, num_kv_heads, head_dim))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                          partition_size=0, num_kv_heads=1) -> int:
+    out = c_sz(0)
+    _check(_lib.pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                         partition_size, num_kv_heads, ctypes.byref(out)))
+    return int(out.value)
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+           partition_size=0, workspace=None, stream=None):
+    """q/out [S, Hq, D]; block_tables int32 [S, stride]; context_lens int32 [S].
+    ``workspace``: uint8 device tensor of decode_workspace_size() bytes."""
+    import torch
+    S, Hq, D = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    need = decode_workspace_size(S, Hq, D, max_context_len, partition_size, Hkv)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
+                          _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
+                          Hkv, D, B, max_context_len, scale, partition_size, _ptr(workspace),
+                          ws_bytes, _dtype_code(q), _stream(stream)))
+    return out
+
+
+def prefill_chunk(out, q, k_cache, v_cache, block_tables, q_start_loc, seq_lens, max_q_len,
+                  max_seq_len, scale, stream=None):
+    """q/out [T, Hq, D] packed; q_start_loc int32 [n+1]; seq_lens int32 [n]."""
+    T, Hq, D = q.shape
+    N, Hkv, B, _ = k_cache.shape
+    _check(_lib.pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(q_start_loc),
+                                 _ptr(seq_lens), seq_lens.shape[0], max_q_len, max_seq_len, Hq,
+                                 Hkv, D, B, scale, _dtype_code(q), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# host block pool
+# ---------------------------------------------------------------------------
+
+class BlockPool:
+    """Refcounted block pool with copy-on-write (host side, ids only)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, seed: int = 0):
+        h = c_vp()
+        _check(_lib.pa_pool_create(num_blocks, block_size, seed, ctypes.byref(h)))
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_free(self) -> int:
+        return int(_lib.pa_pool_num_free(self._h))
+
+    @property
+    def num_blocks(self) -> int:
+        return int(_lib.pa_pool_num_blocks(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.pa_block_refcount(self._h, block))
+
+    def create(self) -> int:
+        sid = c_i64()
+        _check(_lib.pa_seq_create(self._h, ctypes.byref(sid)))
+        return sid.value
+
+    def fork(self, parent: int) -> int:
+        sid = c_i64()
+        _check(_lib.pa_seq_fork(self._h, parent, ctypes.byref(sid)))
+        return sid.value
+
+    def append(self, seq: int, n_tokens: int):
+        """Returns (slots: list[int], cow: list[(src, dst)])."""
+        slots = (c_i64 * max(n_tokens, 1))()
+        cow = (c_i32 * 2)()
+        n_cow = c_i32(0)
+        _check(_lib.pa_seq_append(self._h, seq, n_tokens, slots, cow, 1, ctypes.byref(n_cow)))
+        return list(slots[:n_tokens]), ([(cow[0], cow[1])] if n_cow.value else [])
+
+    def free(self, seq: int):
+        _check(_lib.pa_seq_free(self._h, seq))
+
+    def block_table(self, seq: int):
+        nb, nt = c_i32(), c_i32()
+        _check(_lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(nt)))
+        buf = (c_i32 * max(nb.value, 1))()
+        _check(_lib.pa_seq_block_table(self._h, seq, buf, nb.value, ctypes.byref(nb),
+                                       ctypes.byref(nt)))
+        return list(buf[:nb.value]), nt.value
+
+    def block_tables(self, seqs, stride: int, pad: int = 0):
+        """int32 numpy [len(seqs), stride] block tables and int32 context lengths."""
+        import numpy as np
+        n = len(seqs)
+        ids = np.asarray(seqs, dtype=np.int64)
+        out = np.empty((n, stride), dtype=np.int32)
+        ctx = np.empty(n, dtype=np.int32)
+        _check(_lib.pa_seq_block_tables(self._h, ids.ctypes.data_as(P_i64), n,
+                                        out.ctypes.data_as(P_i32), stride, pad,
+                                        ctx.ctypes.data_as(P_i32)))
+        return out, ctx

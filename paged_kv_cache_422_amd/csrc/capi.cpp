@@ -1,0 +1,333 @@
+// C ABI of libpa (declared in include/pa.h): argument validation, workspace
+// sizing, kernel dispatch and the host block pool.  Every entry point checks
+// its arguments before launching anything and reports failures through
+// pa_status plus a thread-local message; nothing throws across the ABI.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "launch.hpp"
+#include "pool.hpp"
+
+struct pa_pool {
+  pa::BlockPool impl;
+  pa_pool(int32_t n, int32_t b, uint64_t seed) : impl(n, b, seed) {}
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(pa_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+pa_status ok() {
+  g_err.clear();
+  return PA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kBlock = 16;
+constexpr int kMaxPartitionTokens = 1024;   // one block id per lane of a wave64
+
+pa_status check_common(const char* fn, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       pa_dtype dtype) {
+  if (dtype != PA_FP16 && dtype != PA_BF16)
+    return fail(PA_ENOTSUP, std::string(fn) + ": dtype must be PA_FP16 or PA_BF16");
+  if (block_size != kBlock)
+    return fail(PA_ENOTSUP, std::string(fn) + ": block_size must be 16 (got " +
+                                std::to_string(block_size) + ")");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ENOTSUP, std::string(fn) + ": head_dim must be 64 or 128 (got " +
+                                std::to_string(head_dim) + ")");
+  if (num_kv_heads <= 0)
+    return fail(PA_EINVAL, std::string(fn) + ": num_kv_heads must be positive");
+  return PA_OK;
+}
+
+pa_status hip_result(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(PA_EHIP, std::string(fn) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+int32_t resolve_partition(int32_t requested, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim) {
+  return requested > 0 ? requested : pa_default_partition_size(num_q_heads, num_kv_heads, head_dim);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+const char* pa_version(void) { return "libpa 0.1 gfx950"; }
+
+pa_status pa_write_kv(const void* k, const void* v, int64_t src_token_stride, void* k_cache,
+                      void* v_cache, int64_t num_blocks, const int64_t* slot_mapping,
+                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, pa_dtype dtype, void* stream) {
+  const char* fn = "pa_write_kv";
+  if (pa_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype)) return st;
+  if (num_tokens < 0 || num_blocks < 0) return fail(PA_EINVAL, "pa_write_kv: negative size");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_EINVAL, "pa_write_kv: null pointer");
+  if (src_token_stride < static_cast<int64_t>(num_kv_heads) * head_dim)
+    return fail(PA_EINVAL, "pa_write_kv: src_token_stride smaller than num_kv_heads*head_dim");
+  if (src_token_stride % 8 != 0 || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return fail(PA_ENOTSUP, "pa_write_kv: 16-byte alignment required (pointers, stride % 8)");
+  pa::WriteKvArgs a{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                    src_token_stride, static_cast<uint16_t*>(k_cache),
+                    static_cast<uint16_t*>(v_cache), num_blocks, slot_mapping, num_tokens,
+                    num_kv_heads, head_dim};
+  return hip_result(fn, pa::launch_write_kv(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, const int32_t* pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, pa_dtype dtype, void* stream) {
+  const char* fn = "pa_copy_blocks";
+  if (pa_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype)) return st;
+  if (num_pairs < 0 || num_blocks < 0) return fail(PA_EINVAL, "pa_copy_blocks: negative size");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "pa_copy_blocks: null pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ENOTSUP, "pa_copy_blocks: caches must be 16-byte aligned");
+  pa::CopyBlocksArgs a{static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       num_blocks, pairs, num_pairs,
+                       static_cast<int64_t>(num_kv_heads) * block_size * head_dim};
+  return hip_result(fn, pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  (void)num_q_heads;
+  (void)num_kv_heads;
+  (void)head_dim;
+  return 512;
+}
+
+pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_size,
+                                   int32_t num_kv_heads, size_t* bytes) {
+  if (!bytes) return fail(PA_EINVAL, "pa_decode_workspace_size: bytes is null");
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size < 0 || num_kv_heads <= 0)
+    return fail(PA_EINVAL, "pa_decode_workspace_size: bad size");
+  const int32_t P = resolve_partition(partition_size, num_q_heads, num_kv_heads, head_dim);
+  const int64_t max_parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
+  if (max_parts <= 1) {
+    *bytes = 0;
+    return ok();
+  }
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * max_parts;
+  *bytes = static_cast<size_t>(rows) * (head_dim + 2) * sizeof(float);
+  return ok();
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  const char* fn = "pa_decode";
+  if (pa_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype)) return st;
+  if (num_seqs < 0 || num_blocks < 0 || bt_stride <= 0 || max_context_len < 0)
+    return fail(PA_EINVAL, "pa_decode: negative size or bt_stride <= 0");
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "pa_decode: num_q_heads must be a positive multiple of num_kv_heads");
+  if (partition_size != 0 &&
+      (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > kMaxPartitionTokens))
+    return fail(PA_ENOTSUP, "pa_decode: partition_size must be 0 or a multiple of 16 in [16, 1024]");
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_EINVAL, "pa_decode: null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ENOTSUP, "pa_decode: 16-byte alignment required");
+  if (num_seqs > 65535) return fail(PA_ENOTSUP, "pa_decode: at most 65535 sequences per call");
+  const int32_t P = resolve_partition(partition_size, num_q_heads, num_kv_heads, head_dim);
+  size_t need = 0;
+  if (pa_status st = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                              P, num_kv_heads, &need))
+    return st;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_EINVAL, "pa_decode: workspace too small (need " + std::to_string(need) +
+                               " bytes, got " + std::to_string(workspace_bytes) + ")");
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t num_sub = (group + 15) / 16;
+  const int64_t max_parts = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P);
+  if (static_cast<int64_t>(num_kv_heads) * num_sub > 65535)
+    return fail(PA_ENOTSUP, "pa_decode: too many heads");
+  pa::DecodeArgs a{};
+  a.out = static_cast<uint16_t*>(out);
+  float* ws = static_cast<float*>(workspace);
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * max_parts;
+  a.ws_acc = need ? ws : nullptr;
+  a.ws_ml = need ? ws + rows * head_dim : nullptr;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_sub = num_sub;
+  a.part_blocks = P / kBlock;
+  a.max_parts = static_cast<int32_t>(max_parts);
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_result(fn, pa::launch_decode(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                           const int32_t* q_start_loc, const int32_t* seq_lens, int32_t num_chunks,
+                           int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                           pa_dtype dtype, void* stream) {
+  const char* fn = "pa_prefill_chunk";
+  if (pa_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype)) return st;
+  if (num_chunks < 0 || num_blocks < 0 || bt_stride <= 0 || max_q_len < 0 || max_seq_len < 0)
+    return fail(PA_EINVAL, "pa_prefill_chunk: negative size or bt_stride <= 0");
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "pa_prefill_chunk: num_q_heads must be a positive multiple of num_kv_heads");
+  if (num_chunks == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !q_start_loc || !seq_lens)
+    return fail(PA_EINVAL, "pa_prefill_chunk: null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ENOTSUP, "pa_prefill_chunk: 16-byte alignment required");
+  if (num_chunks > 65535) return fail(PA_ENOTSUP, "pa_prefill_chunk: at most 65535 chunks per call");
+  pa::PrefillArgs a{};
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.q_start_loc = q_start_loc;
+  a.seq_lens = seq_lens;
+  a.num_blocks = num_blocks;
+  a.bt_stride = bt_stride;
+  a.num_chunks = num_chunks;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_result(fn, pa::launch_prefill(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// host block pool
+// ---------------------------------------------------------------------------
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed, pa_pool** out) {
+  if (!out) return fail(PA_EINVAL, "pa_pool_create: out is null");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PA_EINVAL, "pa_pool_create: num_blocks and block_size must be positive");
+  pa_pool* p = new (std::nothrow) pa_pool(num_blocks, block_size, seed);
+  if (!p) return fail(PA_ENOMEM, "pa_pool_create: host allocation failed");
+  *out = p;
+  return ok();
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->impl.num_free() : -1; }
+
+int32_t pa_pool_num_blocks(const pa_pool* pool) { return pool ? pool->impl.num_blocks() : -1; }
+
+int32_t pa_block_refcount(const pa_pool* pool, int32_t block) {
+  return pool ? pool->impl.refcount(block) : -1;
+}
+
+pa_status pa_seq_create(pa_pool* pool, int64_t* seq_id) {
+  if (!pool || !seq_id) return fail(PA_EINVAL, "pa_seq_create: null pointer");
+  *seq_id = pool->impl.create();
+  return ok();
+}
+
+pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t* child) {
+  if (!pool || !child) return fail(PA_EINVAL, "pa_seq_fork: null pointer");
+  std::string err;
+  if (pool->impl.fork(parent, child, &err) != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+  return ok();
+}
+
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow) {
+  if (!pool || !n_cow) return fail(PA_EINVAL, "pa_seq_append: null pointer");
+  if (n_tokens > 0 && !slot_mapping_out) return fail(PA_EINVAL, "pa_seq_append: slot_mapping_out is null");
+  if (cow_cap < 1 || !cow_pairs_out)
+    return fail(PA_EINVAL, "pa_seq_append: cow_pairs_out must hold at least one pair");
+  std::string err;
+  int32_t src = -1, dst = -1;
+  const pa::PoolResult r = pool->impl.append(seq, n_tokens, slot_mapping_out, &src, &dst, n_cow, &err);
+  if (r == pa::PoolResult::kNoMemory) return fail(PA_ENOMEM, err);
+  if (r != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+  if (*n_cow) {
+    cow_pairs_out[0] = src;
+    cow_pairs_out[1] = dst;
+  }
+  return ok();
+}
+
+pa_status pa_seq_free(pa_pool* pool, int64_t seq) {
+  if (!pool) return fail(PA_EINVAL, "pa_seq_free: null pool");
+  std::string err;
+  if (pool->impl.release(seq, &err) != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+  return ok();
+}
+
+pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap,
+                             int32_t* n_blocks, int32_t* n_tokens) {
+  if (!pool || !n_blocks || !n_tokens) return fail(PA_EINVAL, "pa_seq_block_table: null pointer");
+  const std::vector<int32_t>* t = pool->impl.table(seq);
+  if (!t) return fail(PA_EINVAL, "pa_seq_block_table: unknown sequence " + std::to_string(seq));
+  *n_blocks = static_cast<int32_t>(t->size());
+  *n_tokens = static_cast<int32_t>(pool->impl.num_tokens(seq));
+  if (cap > 0 && !out) return fail(PA_EINVAL, "pa_seq_block_table: out is null");
+  const int32_t n = std::min<int32_t>(cap, *n_blocks);
+  if (n > 0) std::memcpy(out, t->data(), sizeof(int32_t) * n);
+  return ok();
+}
+
+pa_status pa_seq_block_tables(const pa_pool* pool, const int64_t* seq_ids, int32_t n, int32_t* out,
+                              int32_t stride, int32_t pad, int32_t* ctx_out) {
+  if (!pool || (n > 0 && (!seq_ids || !out))) return fail(PA_EINVAL, "pa_seq_block_tables: null pointer");
+  if (n < 0 || stride <= 0) return fail(PA_EINVAL, "pa_seq_block_tables: bad size");
+  for (int32_t i = 0; i < n; ++i) {
+    const std::vector<int32_t>* t = pool->impl.table(seq_ids[i]);
+    if (!t) return fail(PA_EINVAL, "pa_seq_block_tables: unknown sequence " + std::to_string(seq_ids[i]));
+    if (static_cast<int64_t>(t->size()) > stride)
+      return fail(PA_EINVAL, "pa_seq_block_tables: table longer than stride");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const std::vector<int32_t>* t = pool->impl.table(seq_ids[i]);
+    int32_t* row = out + static_cast<int64_t>(i) * stride;
+    const int32_t nb = static_cast<int32_t>(t->size());
+    if (nb) std::memcpy(row, t->data(), sizeof(int32_t) * nb);
+    for (int32_t j = nb; j < stride; ++j) row[j] = pad;
+    if (ctx_out) ctx_out[i] = static_cast<int32_t>(pool->impl.num_tokens(seq_ids[i]));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,322 @@
+// Paged decode attention for gfx950 (MI355X).
+//
+// One query token per sequence attends to every key of its sequence; the keys
+// and values sit in 16-token blocks scattered through the pool and are found
+// through the sequence's block table, so the kernel reads the blocks "as if
+// contiguous" ("Inside vLLM: How PagedAttention Changes Python LLM Inference
+// at the Systems Level", section "PagedAttention: What the OS Figured Out
+// Decades Ago").  Decode is bound by memory bandwidth ("PagedAttention in
+// vLLM: A Throughput Settings Guide", section "Continuous Batching Keeps the
+// GPU Busy"): every K/V byte of the batch is read exactly once per step, so
+// the roofline is HBM and the design goal is to keep enough bytes in flight.
+//
+// Work split (library design, not from the pages): a sequence's context is
+// cut into partitions of part_blocks blocks.  One 256-thread workgroup
+// (4 wave64s) handles one (sequence, KV head, partition) for all query heads
+// of that KV head's group, so K/V are read once per group.  Wave w takes
+// blocks w, w+4, ... of the partition; waves merge through LDS.  A sequence
+// with one partition writes its output directly; otherwise each partition
+// writes (max, sum, unnormalised accumulator) and a second kernel merges them
+// by log-sum-exp.  The order of every reduction depends only on the
+// sequence's own length and the partition size, so the result for a sequence
+// does not depend on the rest of the batch or on where its blocks live.
+//
+// Per 16-token block a wave does (16 = MFMA tile edge = block size):
+//   S^T[16 keys x 16 heads] = K[16 x D] . Q^T[D x 16]    (D/32 MFMA 16x16x32)
+//   online softmax in registers (scores in log2 units, fp32)
+//   O[16 heads x D] += P[16 x 16 keys] . V[16 keys x D]  (D/16 MFMA 16x16x16)
+// The accumulator layout of the first product is exactly the operand layout
+// the second needs for P, so probabilities never leave registers.  V is stored
+// dim-major per block, which makes the V operand an 8-byte load per lane.
+// Query-head columns beyond the group size are zero padding.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pa {
+
+namespace {
+
+constexpr int kBlock = 16;   // tokens per KV block == MFMA tile edge
+constexpr int kWaves = 4;
+
+// -1: invalid context length; 0: empty; otherwise number of partitions.
+__device__ __forceinline__ int num_partitions(int L, const DecodeArgs& a) {
+  if (L < 0 || L > a.max_context_len || L > a.bt_stride * kBlock) return -1;
+  const int P = a.part_blocks * kBlock;
+  return (L + P - 1) / P;
+}
+
+template <class T, int D>
+struct BlockRegs {
+  u32x4 k[D / 32];   // K rows: key lane%16, dims 32*ks + 8*(lane/16) .. +7
+  u32x2 v[D / 16];   // V: dim 16*t + lane%16, keys 4*(lane/16) .. +3
+};
+
+template <class T, int D>
+__device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* kbase,
+                                           const uint16_t* vbase, int64_t off) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    r.k[ks] = *reinterpret_cast<const u32x4*>(kbase + off + 32 * ks);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    r.v[t] = *reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t);
+}
+
+template <class T, int D, int NH>
+__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int VT = D / 16;
+  __shared__ float sm_m[kWaves][NH];
+  __shared__ float sm_l[kWaves][NH];
+  __shared__ float sm_o[kWaves][NH][D];
+
+  const int part = blockIdx.x;
+  const int s = blockIdx.y;
+  const int g = blockIdx.z / a.num_sub;
+  const int sub = blockIdx.z - g * a.num_sub;
+  const int hq0 = g * a.group + sub * 16;
+  const int nh = min(16, a.group - sub * 16);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 15;
+  const int quad = lane >> 4;
+
+  const int L = a.context_lens[s];
+  const int np = num_partitions(L, a);
+  if (np <= 0) {
+    // Empty context: zero rows.  Invalid length: NaN rows.  Partition 0 only.
+    if (part == 0) {
+      const uint16_t fill = np == 0 ? uint16_t(0) : from_f32<T>(NAN);
+      for (int i = tid; i < nh * D; i += 256)
+        a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + i / D) * D + i % D] = fill;
+    }
+    return;
+  }
+  if (part >= np) return;
+
+  const int blk0 = part * a.part_blocks;
+  const int nblk = min(a.part_blocks, (L + kBlock - 1) / kBlock - blk0);
+
+  // This partition's block ids, one per lane (part_blocks <= 64).
+  int my_bt = 0;
+  if (lane < nblk) my_bt = a.block_tables[static_cast<int64_t>(s) * a.bt_stride + blk0 + lane];
+  const bool bad_id = lane < nblk && (my_bt < 0 || my_bt >= a.num_blocks);
+  const bool poison = __any(bad_id);
+  if (bad_id) my_bt = 0;
+
+  // Q^T operand: head column hl, dims 32*ks + 8*quad .. +7 (zero padding
+  // columns beyond the group).
+  u32x4 qb[KS];
+  if (hl < nh) {
+    const uint16_t* qp = a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0 + hl) * D + 8 * quad;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * D + 8 * quad;
+  const uint16_t* vbase = a.v_cache + g * tile_elems + hl * kBlock + 4 * quad;
+
+  float m_run = -INFINITY;   // running max of this lane's head (log2 units)
+  float l_run = 0.f;         // this lane's share of the running sum
+  f32x4 o[VT];
+#pragma unroll
+  for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  BlockRegs<T, D> cur, nxt;
+  int j = w;
+  if (j < nblk) load_block<T, D>(cur, kbase, vbase, __builtin_amdgcn_readlane(my_bt, j) * blk_elems);
+  for (; j < nblk; j += kWaves) {
+    const int jn = j + kWaves;
+    if (jn < nblk) load_block<T, D>(nxt, kbase, vbase, __builtin_amdgcn_readlane(my_bt, jn) * blk_elems);
+
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sacc = mfma16x16x32<T>(cur.k[ks], qb[ks], sacc);
+
+    const int n_valid = L - (blk0 + j) * kBlock;   // >= 1
+    float sc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sc[e] = (4 * quad + e < n_valid) ? sacc[e] * a.scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = fast_exp2(m_run - m_new);
+    uint16_t pb[4], pl[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = fast_exp2(sc[e] - m_new);
+      pb[e] = from_f32<T>(pe);
+      float pr = to_f32<T>(pb[e]);
+      if constexpr (SplitP<T>::kSplit) {
+        pl[e] = from_f32<T>(pe - pr);
+        pr += to_f32<T>(pl[e]);
+      }
+      psum += pr;   // the sum uses the same rounded weights as P.V
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // Output rows are heads 4*quad + e; their rescale factors live in lanes
+    // whose column (lane % 16) is that head.
+    float ar[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * quad + e);
+
+    if (n_valid < kBlock) {
+      // Keys past the end hold stale data (possibly NaN): zero them.
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        uint32_t lo = cur.v[t][0], hi = cur.v[t][1];
+        const int k0 = 4 * quad;
+        if (k0 + 0 >= n_valid) lo &= 0xffff0000u;
+        if (k0 + 1 >= n_valid) lo &= 0x0000ffffu;
+        if (k0 + 2 >= n_valid) hi &= 0xffff0000u;
+        if (k0 + 3 >= n_valid) hi &= 0x0000ffffu;
+        cur.v[t] = u32x2{lo, hi};
+      }
+    }
+    const u32x2 pa = {pack2(pb[0], pb[1]), pack2(pb[2], pb[3])};
+    const u32x2 pal = {pack2(pl[0], pl[1]), pack2(pl[2], pl[3])};
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      f32x4 c = o[t];
+      c[0] *= ar[0];
+      c[1] *= ar[1];
+      c[2] *= ar[2];
+      c[3] *= ar[3];
+      c = mfma16x16x16<T>(pa, cur.v[t], c);
+      if constexpr (SplitP<T>::kSplit) c = mfma16x16x16<T>(pal, cur.v[t], c);
+      o[t] = c;
+    }
+    cur = nxt;
+  }
+
+  // Per-head sums over the four key groups of the wave.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (lane < NH) {
+    sm_m[w][lane] = m_run;
+    sm_l[w][lane] = l_run;
+  }
+#pragma unroll
+  for (int t = 0; t < VT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int h = 4 * quad + e;
+      if (h < NH) sm_o[w][h][16 * t + hl] = o[t][e];
+    }
+  __syncthreads();
+
+  for (int i = tid; i < nh * D; i += 256) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][h]);
+    float lsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float f = fast_exp2(sm_m[v][h] - M);
+      lsum += sm_l[v][h] * f;
+      acc += sm_o[v][h][d] * f;
+    }
+    if (poison) acc = NAN;
+    const int64_t row = static_cast<int64_t>(s) * a.num_q_heads + hq0 + h;
+    if (np == 1) {
+      a.out[row * D + d] = from_f32<T>(acc / lsum);
+    } else {
+      const int64_t slot = row * a.max_parts + part;
+      a.ws_acc[slot * D + d] = acc;
+      if (d == 0) {
+        a.ws_ml[slot * 2] = M;
+        a.ws_ml[slot * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Second pass: one wave per (sequence, query head) with more than one
+// partition.  m = max_p m_p; l = sum_p l_p 2^(m_p - m);
+// o = sum_p acc_p 2^(m_p - m) / l, partitions in index order.
+template <class T, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= static_cast<int64_t>(a.num_seqs) * a.num_q_heads) return;
+  const int s = static_cast<int>(row / a.num_q_heads);
+  const int np = num_partitions(a.context_lens[s], a);
+  if (np <= 1) return;
+  const float* ml = a.ws_ml + row * a.max_parts * 2;
+  const float* acc = a.ws_acc + row * a.max_parts * D;
+  float M = -INFINITY;
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
+  M = wave_max(M);
+  float lsum = 0.f;
+  for (int p = lane; p < np; p += 64) lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  lsum = wave_sum(lsum);
+  constexpr int PER = D / 64;
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float f = fast_exp2(ml[2 * p] - M);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] += acc[static_cast<int64_t>(p) * D + lane + 64 * i] * f;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) a.out[row * D + lane + 64 * i] = from_f32<T>(o[i] / lsum);
+}
+
+template <class T, int D, int NH>
+hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.max_parts, a.num_seqs, a.num_kv_heads * a.num_sub);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, NH>), grid, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(static_cast<uint32_t>((rows + 3) / 4)),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  const int nh = a.group < 16 ? a.group : 16;
+  if (nh <= 1) return launch_nh<T, D, 1>(a, stream);
+  if (nh <= 2) return launch_nh<T, D, 2>(a, stream);
+  if (nh <= 4) return launch_nh<T, D, 4>(a, stream);
+  if (nh <= 8) return launch_nh<T, D, 8>(a, stream);
+  return launch_nh<T, D, 16>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  if (dtype == 0) return head_dim == 64 ? launch_d<F16, 64>(a, stream) : launch_d<F16, 128>(a, stream);
+  return head_dim == 64 ? launch_d<BF16, 64>(a, stream) : launch_d<BF16, 128>(a, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,164 @@
+"""Paged decode parity against the fp64 oracle, plus the GPU-side invariants:
+block-permutation and batch invariance (bit-exact), partition-size
+invariance (tolerance), stale/NaN slots never leak, edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode
+from workloads import llama7b, llama8b_gqa, tiny
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_decode(q, kc, vc, bt, ctx, scale, seqs=None):
+    return A.decode(bits(q), bits(kc), bits(vc), bt, ctx, scale, dtype_name(q), seqs=seqs)
+
+
+def small_case(S, Hq, Hkv, D, dtype, lens, seed=0, extra_blocks=4):
+    """Random scattered layout; unused slots and the pad block hold NaN."""
+    rng = np.random.default_rng(seed)
+    nb = [-(-int(L) // 16) for L in lens]
+    N = sum(nb) + extra_blocks
+    perm = rng.permutation(N).astype(np.int32)
+    pad = int(perm[-1])
+    stride = max(max(nb), 1) + 2
+    bt = np.full((S, stride), pad, np.int32)
+    at = 0
+    for s, n in enumerate(nb):
+        bt[s, :n] = perm[at:at + n]
+        at += n
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    q = torch.randn(S, Hq, D, generator=g, device=DEV).to(dtype)
+    kc = torch.randn(N, Hkv, 16, D, generator=g, device=DEV).to(dtype)
+    vc = torch.randn(N, Hkv, D, 16, generator=g, device=DEV).to(dtype)
+    # poison every slot no sequence owns
+    for s, L in enumerate(lens):
+        if L % 16:
+            kc[int(bt[s, nb[s] - 1]), :, L % 16:, :] = float("nan")
+            vc[int(bt[s, nb[s] - 1]), :, :, L % 16:] = float("nan")
+    for b in perm[at:]:
+        kc[int(b)] = float("nan")
+        vc[int(b)] = float("nan")
+    return q, kc, vc, bt, np.asarray(lens, np.int32)
+
+
+def test_tiny_workload():
+    w = tiny()
+    print("tiny workload", flush=True)
+    q, kc, vc = (t.to(DEV) for t in w.make_tensors("cpu"))
+    out = run_decode(q, kc, vc, w.block_tables, w.context_lens, w.max_model_len, w.scale)
+    want = oracle_decode(q, kc, vc, w.block_tables, w.context_lens, w.scale)
+    assert_close(out, want, what="tiny")
+    # L = 1: the output is V_0 rounded (exact: one weight of 1.0)
+    assert w.context_lens[0] == 1
+    assert np.array_equal(out[0].float().cpu().numpy(), want[0].astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (8, 2, 128), (32, 8, 128), (16, 1, 64),
+                                      (40, 40, 128), (32, 1, 128), (6, 2, 64)])
+@pytest.mark.parametrize("P", [0, 16, 256])
+def test_decode_shapes(dtype, Hq, Hkv, D, P):
+    lens = [1, 15, 16, 17, 100, 511, 512, 513, 1030]
+    print(f"decode dtype={dtype} Hq={Hq} Hkv={Hkv} D={D} P={P}", flush=True)
+    q, kc, vc, bt, ctx = small_case(len(lens), Hq, Hkv, D, dtype, lens, seed=Hq + D + P)
+    out = run_decode(q, kc, vc, bt, ctx, max(lens), 1 / math.sqrt(D), P)
+    want = oracle_decode(q, kc, vc, bt, ctx, 1 / math.sqrt(D))
+    assert_close(out, want, what=f"Hq={Hq} Hkv={Hkv} D={D} P={P}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_few_keys(dtype):
+    """Contexts of 2-9 keys: the softmax rests on a handful of weights, so the
+    16-bit rounding of probabilities is not averaged away."""
+    lens = list(range(2, 10)) * 8
+    q, kc, vc, bt, ctx = small_case(len(lens), 32, 8, 128, dtype, lens, seed=31)
+    out = run_decode(q, kc, vc, bt, ctx, 16, 1 / math.sqrt(128), 0)
+    assert_close(out, oracle_decode(q, kc, vc, bt, ctx, 1 / math.sqrt(128)), what="few keys")
+
+
+def test_empty_and_invalid_lengths():
+    lens = [0, 40, 5, 0]
+    q, kc, vc, bt, ctx = small_case(4, 8, 2, 128, torch.bfloat16, [1, 40, 5, 1], seed=3)
+    ctx = np.array(lens, np.int32)
+    out = run_decode(q, kc, vc, bt, ctx, 64, 0.1, 16)
+    o = out.float().cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(o[3] == 0)
+    want = oracle_decode(q, kc, vc, bt, ctx, 0.1)
+    assert_close(out, want, what="empty rows")
+    # a length above max_context_len gives NaN rows, others unaffected
+    ctx2 = np.array([0, 40, 100, 5], np.int32)
+    out2 = run_decode(q, kc, vc, bt, ctx2, 64, 0.1, 16)
+    o2 = out2.float().cpu().numpy()
+    assert np.all(np.isnan(o2[2])) and np.all(o2[0] == 0)
+    assert np.array_equal(o2[1], o[1])
+
+
+def test_out_of_range_block_id_poisons_only_that_sequence():
+    q, kc, vc, bt, ctx = small_case(3, 4, 4, 64, torch.float16, [20, 33, 7], seed=4)
+    good = run_decode(q, kc, vc, bt, ctx, 64, 0.125, 16)
+    bt2 = bt.copy()
+    bt2[1, 1] = kc.shape[0] + 5
+    bad = run_decode(q, kc, vc, bt2, ctx, 64, 0.125, 16)
+    b = bad.float().cpu().numpy()
+    assert np.all(np.isnan(b[1]))
+    assert np.array_equal(b[[0, 2]], good.float().cpu().numpy()[[0, 2]])
+
+
+def test_unit_values_give_unit_output():
+    """Softmax weights sum to one through the partition merge (V == 1)."""
+    lens = [700, 1500, 33]
+    q, kc, vc, bt, ctx = small_case(3, 32, 8, 128, torch.bfloat16, lens, seed=9)
+    vc.fill_(1.0)
+    out = run_decode(q, kc, vc, bt, ctx, 2048, 0.088, 256)
+    assert torch.all(out.float() == 1.0)
+
+
+def test_block_permutation_is_bit_exact():
+    lens = [300, 47, 1024, 900]
+    q, kc, vc, bt, ctx = small_case(4, 32, 8, 128, torch.bfloat16, lens, seed=12)
+    base = run_decode(q, kc, vc, bt, ctx, 1024, 0.088, 256)
+    N = kc.shape[0]
+    pi = torch.from_numpy(np.random.default_rng(1).permutation(N)).to(DEV)
+    kc2 = torch.empty_like(kc); vc2 = torch.empty_like(vc)
+    kc2[pi] = kc; vc2[pi] = vc
+    bt2 = pi.cpu().numpy()[bt].astype(np.int32)
+    again = run_decode(q, kc2, vc2, bt2, ctx, 1024, 0.088, 256)
+    assert torch.equal(base.view(torch.int16), again.view(torch.int16))
+
+
+def test_batch_invariance_is_bit_exact():
+    lens = [1200, 64, 3000, 17, 555]
+    q, kc, vc, bt, ctx = small_case(5, 32, 8, 128, torch.float16, lens, seed=13)
+    full = run_decode(q, kc, vc, bt, ctx, 4096, 0.088, 512)
+    for s in (0, 2, 4):
+        one = run_decode(q[s:s + 1].contiguous(), kc, vc, bt[s:s + 1], ctx[s:s + 1], 4096, 0.088, 512)
+        assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16))
+
+
+def test_partition_size_changes_only_rounding():
+    lens = [2000, 1500, 999]
+    q, kc, vc, bt, ctx = small_case(3, 8, 8, 128, torch.float16, lens, seed=14)
+    want = oracle_decode(q, kc, vc, bt, ctx, 0.088)
+    for P in (16, 128, 512, 1024):
+        assert_close(run_decode(q, kc, vc, bt, ctx, 2048, 0.088, P), want, what=f"P={P}")
+
+
+@pytest.mark.parametrize("make", [llama7b, llama8b_gqa], ids=["llama7b", "llama8b_gqa"])
+def test_full_size_workloads(make):
+    """The benchmark workloads at full size, default/benchmark partitioning,
+    every sequence checked against the oracle."""
+    w = make()
+    print(f"{w.name}: S={w.num_seqs} blocks={w.num_blocks}", flush=True)
+    q, kc, vc = w.make_tensors(DEV)
+    out = run_decode(q, kc, vc, w.block_tables, w.context_lens, w.max_model_len, w.scale,
+                     w.partition_size)
+    print("  kernel done, running oracle", flush=True)
+    want = A.decode(bits(q), bits(kc), bits(vc), w.block_tables, w.context_lens, w.scale,
+                    w.dtype)
+    r = assert_close(out, want, what=w.name)
+    print(f"  worst err/bound {r:.3f}", flush=True)

@@ -1,0 +1,157 @@
+"""Chunked-prefill parity against the fp64 oracle, and the mixed step
+(slot-mapped write, prefill chunks, decode) end to end."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_422_amd as pa
+from oracle import attention as A
+from oracle import kv_cache as KC
+from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode
+from workloads import mixed
+
+pytestmark = pytest.mark.gpu
+
+
+def prefill_case(chunks, Hq, Hkv, D, dtype, seed=0):
+    """chunks: list of (n_cached, n).  Scattered layout, NaN in unused slots."""
+    rng = np.random.default_rng(seed)
+    lens = [c + n for c, n in chunks]
+    nb = [-(-L // 16) for L in lens]
+    N = sum(nb) + 3
+    perm = rng.permutation(N).astype(np.int32)
+    stride = max(nb) + 1
+    bt = np.full((len(chunks), stride), int(perm[-1]), np.int32)
+    at = 0
+    for c, n in enumerate(nb):
+        bt[c, :n] = perm[at:at + n]
+        at += n
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    T = sum(n for _, n in chunks)
+    q = torch.randn(T, Hq, D, generator=g, device=DEV).to(dtype)
+    kc = torch.randn(N, Hkv, 16, D, generator=g, device=DEV).to(dtype)
+    vc = torch.randn(N, Hkv, D, 16, generator=g, device=DEV).to(dtype)
+    for c, L in enumerate(lens):
+        if L % 16:
+            kc[int(bt[c, nb[c] - 1]), :, L % 16:, :] = float("nan")
+            vc[int(bt[c, nb[c] - 1]), :, :, L % 16:] = float("nan")
+    for b in perm[at:]:
+        kc[int(b)] = float("nan")
+        vc[int(b)] = float("nan")
+    qsl = np.concatenate([[0], np.cumsum([n for _, n in chunks])]).astype(np.int32)
+    return q, kc, vc, bt, qsl, np.asarray(lens, np.int32)
+
+
+def run_prefill(q, kc, vc, bt, qsl, lens, scale):
+    out = torch.full_like(q, float("nan"))
+    n_max = int(np.max(np.diff(qsl)))
+    pa.prefill_chunk(out, q, kc, vc, torch.from_numpy(bt).to(DEV), torch.from_numpy(qsl).to(DEV),
+                     torch.from_numpy(lens).to(DEV), n_max, int(lens.max()), scale)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (4, 4, 64), (8, 2, 64), (12, 4, 128), (3, 1, 128)])
+def test_prefill_shapes(dtype, Hq, Hkv, D):
+    chunks = [(0, 1), (0, 45), (17, 64), (1024 - 40, 97), (5, 200), (33, 16)]
+    print(f"prefill dtype={dtype} Hq={Hq} Hkv={Hkv} D={D}", flush=True)
+    q, kc, vc, bt, qsl, lens = prefill_case(chunks, Hq, Hkv, D, dtype, seed=Hq * D)
+    scale = 1 / math.sqrt(D)
+    out = run_prefill(q, kc, vc, bt, qsl, lens, scale)
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, scale, dtype_name(q))
+    assert_close(out, want, what=f"prefill Hq={Hq} Hkv={Hkv} D={D}")
+
+
+def test_prefill_chunking_and_decode_agree():
+    """Rows computed as one chunk, as two chunks, and the last row as a
+    decode step all agree within tolerance of the oracle."""
+    dtype, Hq, Hkv, D, L = torch.bfloat16, 32, 8, 128, 300
+    q, kc, vc, bt, qsl, lens = prefill_case([(0, L)], Hq, Hkv, D, dtype, seed=21)
+    scale = 1 / math.sqrt(D)
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, scale, "bf16")
+    one = run_prefill(q, kc, vc, bt, qsl, lens, scale)
+    assert_close(one, want, what="one chunk")
+    cut = 111
+    first = run_prefill(q[:cut].contiguous(), kc, vc, bt, np.array([0, cut], np.int32),
+                        np.array([cut], np.int32), scale)
+    second = run_prefill(q[cut:].contiguous(), kc, vc, bt, np.array([0, L - cut], np.int32),
+                         np.array([L], np.int32), scale)
+    assert_close(torch.cat([first, second]), want, what="two chunks")
+    dec = run_decode(q[-1:].contiguous(), kc, vc, bt, np.array([L], np.int32), L, scale, 0)
+    assert_close(dec, want[-1:], what="decode of the last row")
+
+
+def _mixed_step(w, kc, vc, k_new, v_new, q_dec, q_pre):
+    """write_kv -> prefill chunks -> decode, on the current stream."""
+    sm = torch.from_numpy(w.slot_mapping).to(DEV)
+    pa.write_kv(k_new, v_new, kc, vc, sm)
+    out_pre = torch.full_like(q_pre, float("nan"))
+    pa.prefill_chunk(out_pre, q_pre, kc, vc, torch.from_numpy(w.prefill_bt).to(DEV),
+                     torch.from_numpy(w.q_start_loc).to(DEV),
+                     torch.from_numpy(w.prefill_seq_lens).to(DEV), w.prefill_chunk,
+                     w.prefill_cached + w.prefill_chunk, w.scale)
+    out_dec = torch.full_like(q_dec, float("nan"))
+    pa.decode(out_dec, q_dec, kc, vc, torch.from_numpy(w.decode_bt).to(DEV),
+              torch.from_numpy(w.decode_lens).to(DEV), w.max_model_len, w.scale, w.partition_size)
+    torch.cuda.synchronize()
+    return out_pre, out_dec
+
+
+def _oracle_mixed(w, kc0, vc0, k_new, v_new, q_dec, q_pre, dec_seqs, pre_rows):
+    """Oracle on host copies of the pre-step caches: apply the write, then
+    attention for the sampled decode sequences and prefill rows."""
+    kh, vh = kc0.copy(), vc0.copy()
+    KC.write_kv(kh, vh, bits(k_new), bits(v_new), w.slot_mapping, 16)
+    pre = A.prefill(bits(q_pre), kh, vh, w.prefill_bt, w.q_start_loc, w.prefill_seq_lens,
+                    w.scale, w.dtype, rows=pre_rows)
+    dec = A.decode(bits(q_dec), kh, vh, w.decode_bt, w.decode_lens, w.scale, w.dtype,
+                   seqs=dec_seqs)
+    return pre, dec
+
+
+def test_mixed_step_small():
+    w = mixed(num_decode=96, chunk=300, cached=77, lmin=1, lmax=1200)
+    print(f"mixed small: blocks={w.num_blocks}", flush=True)
+    kc, vc, k_new, v_new, q_dec, q_pre = w.make_tensors(DEV)
+    kc0, vc0 = bits(kc), bits(vc)
+    out_pre, out_dec = _mixed_step(w, kc, vc, k_new, v_new, q_dec, q_pre)
+    pre, dec = _oracle_mixed(w, kc0, vc0, k_new, v_new, q_dec, q_pre, None, None)
+    assert_close(out_pre, pre, what="mixed prefill")
+    assert_close(out_dec, dec, what="mixed decode")
+
+
+def test_mixed_step_full_size_sampled():
+    """The full 8192-token step (44 GB pool); oracle on sampled sequences and
+    rows, copying back only their blocks."""
+    w = mixed()
+    print(f"mixed full: blocks={w.num_blocks}", flush=True)
+    kc, vc, k_new, v_new, q_dec, q_pre = w.make_tensors(DEV)
+    rng = np.random.default_rng(99)
+    dec_seqs = sorted(rng.choice(w.num_decode, 48, replace=False).tolist())
+    pre_rows = sorted(rng.choice(w.num_chunks * w.prefill_chunk, 48, replace=False).tolist())
+    need = set()
+    for s in dec_seqs:
+        need.update(w.decode_bt[s, :-(-int(w.decode_lens[s]) // 16)].tolist())
+    for c in range(w.num_chunks):
+        need.update(w.prefill_bt[c, :-(-int(w.prefill_seq_lens[c]) // 16)].tolist())
+    need = np.array(sorted(need), dtype=np.int64)
+    remap = {int(b): i for i, b in enumerate(need)}
+    idx = torch.from_numpy(need).to(DEV)
+    kc_s, vc_s = bits(kc[idx]), bits(vc[idx])          # pre-step copies of the needed blocks
+    out_pre, out_dec = _mixed_step(w, kc, vc, k_new, v_new, q_dec, q_pre)
+    print("  kernels done, running oracle", flush=True)
+    # Re-express the workload over the compacted block set for the oracle.
+    sm = np.array([remap.get(int(s) // 16, -1) * 16 + int(s) % 16 if int(s) // 16 in remap else -1
+                   for s in w.slot_mapping], dtype=np.int64)
+    dbt = np.vectorize(lambda b: remap.get(int(b), 0))(w.decode_bt).astype(np.int32)
+    pbt = np.vectorize(lambda b: remap.get(int(b), 0))(w.prefill_bt).astype(np.int32)
+    kh, vh = kc_s.copy(), vc_s.copy()
+    KC.write_kv(kh, vh, bits(k_new), bits(v_new), sm, 16)
+    pre = A.prefill(bits(q_pre), kh, vh, pbt, w.q_start_loc, w.prefill_seq_lens, w.scale,
+                    w.dtype, rows=pre_rows)
+    dec = A.decode(bits(q_dec), kh, vh, dbt, w.decode_lens, w.scale, w.dtype, seqs=dec_seqs)
+    assert_close(out_pre[pre_rows], pre[pre_rows], what="full mixed prefill (sampled rows)")
+    assert_close(out_dec[dec_seqs], dec[dec_seqs], what="full mixed decode (sampled seqs)")

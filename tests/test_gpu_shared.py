@@ -1,0 +1,76 @@
+"""Prefix sharing through the refcounted pool with copy-on-write: the cache is
+built by the library's pool, block copies and slot-mapped writes; decode over
+it must match the oracle on the *logical* per-sequence K/V (no layout at all)
+and be bit-identical to decode over private copies."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_422_amd as pa
+from oracle import attention as A
+from tests.gpu_util import DEV, assert_close, bits, run_decode
+from workloads import llama13b_shared
+
+pytestmark = pytest.mark.gpu
+
+
+def build_cache(w, k_tok, v_tok, share: bool, seed: int):
+    """Lay the workload out through the pool.  share=True: each group's prompt
+    prefix is appended once and forked; False: every sequence writes all of
+    its own tokens."""
+    pool = pa.BlockPool(w.num_blocks, 16, seed)
+    H, D = w.num_kv_heads, w.head_dim
+    kc = torch.full((w.num_blocks, H, 16, D), float("nan"), dtype=k_tok.dtype, device=DEV)
+    vc = torch.full((w.num_blocks, H, D, 16), float("nan"), dtype=k_tok.dtype, device=DEV)
+    seqs = [None] * w.num_seqs
+    n_cow = 0
+
+    def write(seq_idx, sid, lo, hi):
+        nonlocal n_cow
+        slots, cow = pool.append(sid, hi - lo)
+        if cow:
+            n_cow += 1
+            pa.copy_blocks(kc, vc, torch.tensor(cow, dtype=torch.int32, device=DEV))
+        rows = torch.from_numpy(w.token_rows[seq_idx][lo:hi]).to(DEV)
+        pa.write_kv(k_tok[rows], v_tok[rows], kc, vc,
+                    torch.tensor(slots, dtype=torch.int64, device=DEV))
+
+    G = w.group_size
+    for k in range(w.num_seqs // G):
+        P = int(w.prefix_lens[k])
+        members = list(range(k * G, (k + 1) * G))
+        if share:
+            root = pool.create()
+            write(members[0], root, 0, P)
+            seqs[members[0]] = root
+            for s in members[1:]:
+                seqs[s] = pool.fork(root)
+            for s in members:
+                write(s, seqs[s], P, int(w.context_lens[s]))
+        else:
+            for s in members:
+                seqs[s] = pool.create()
+                write(s, seqs[s], 0, int(w.context_lens[s]))
+    bt, ctx = pool.block_tables(seqs, w.bt_stride, pad=0)
+    assert np.array_equal(ctx, w.context_lens)
+    torch.cuda.synchronize()
+    return kc, vc, bt, pool, n_cow
+
+
+@pytest.mark.parametrize("full", [False, True], ids=["small", "full"])
+def test_shared_prefix_decode(full):
+    w = llama13b_shared() if full else llama13b_shared(num_seqs=16, num_heads=8, max_len=700)
+    print(f"shared: S={w.num_seqs} H={w.num_q_heads} rows={w.num_token_rows}", flush=True)
+    q, k_tok, v_tok = w.make_tensors(DEV)
+    kc_s, vc_s, bt_s, pool_s, n_cow = build_cache(w, k_tok, v_tok, share=True, seed=7)
+    kc_p, vc_p, bt_p, pool_p, _ = build_cache(w, k_tok, v_tok, share=False, seed=8)
+    # sharing saves blocks; copy-on-write happened for partial prefix blocks
+    assert pool_s.num_free > pool_p.num_free
+    assert n_cow > 0
+    out_s = run_decode(q, kc_s, vc_s, bt_s, w.context_lens, w.max_model_len, w.scale)
+    out_p = run_decode(q, kc_p, vc_p, bt_p, w.context_lens, w.max_model_len, w.scale)
+    assert torch.equal(out_s.view(torch.int16), out_p.view(torch.int16))
+    kt, vt = bits(k_tok), bits(v_tok)
+    want = A.decode_logical(bits(q), [kt[r] for r in w.token_rows], [vt[r] for r in w.token_rows],
+                            w.scale, w.dtype)
+    assert_close(out_s, want, what="shared prefix")

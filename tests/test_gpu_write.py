@@ -1,0 +1,73 @@
+"""Bit-exact parity of the KV write path and copy-on-write block copies."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_422_amd as pa
+from oracle import kv_cache as KC
+from tests.gpu_util import DEV, bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _sentinel_cache(N, H, D, dtype):
+    k = torch.full((N, H, 16, D), 0, dtype=torch.int16, device=DEV)
+    v = torch.full((N, H, D, 16), 0, dtype=torch.int16, device=DEV)
+    k.fill_(-21555)   # 0xABCD pattern
+    v.fill_(-21555)
+    return k.view(dtype), v.view(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("H,D", [(8, 128), (4, 64), (1, 128)])
+def test_write_kv_bit_exact(dtype, H, D):
+    print(f"write_kv dtype={dtype} H={H} D={D}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    N, T = 40, 300
+    kc, vc = _sentinel_cache(N, H, D, dtype)
+    kc0, vc0 = bits(kc), bits(vc)
+    k = torch.randn(T, H, D, generator=g, device=DEV).to(dtype)
+    v = torch.randn(T, H, D, generator=g, device=DEV).to(dtype)
+    rng = np.random.default_rng(5)
+    slots = rng.permutation(N * 16)[:T].astype(np.int64)
+    slots[::7] = -1                     # skipped tokens
+    slots[5] = N * 16 + 3               # out of range: skipped too
+    sm = torch.from_numpy(slots).to(DEV)
+    pa.write_kv(k, v, kc, vc, sm)
+    torch.cuda.synchronize()
+    want_k, want_v = kc0.copy(), vc0.copy()
+    slots_ok = np.where(slots < N * 16, slots, -1)
+    KC.write_kv(want_k, want_v, bits(k), bits(v), slots_ok, 16)
+    assert np.array_equal(bits(kc).view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(bits(vc).view(np.uint16), want_v.view(np.uint16))
+
+
+def test_write_kv_strided_source():
+    """k/v as views into a fused [T, 3, H, D] tensor (token stride 3*H*D)."""
+    dtype, H, D, N, T = torch.bfloat16, 8, 128, 16, 50
+    g = torch.Generator(device=DEV).manual_seed(3)
+    qkv = torch.randn(T, 3, H, D, generator=g, device=DEV).to(dtype)
+    k, v = qkv[:, 1], qkv[:, 2]
+    kc, vc = _sentinel_cache(N, H, D, dtype)
+    want_k, want_v = bits(kc), bits(vc)
+    slots = np.random.default_rng(1).permutation(N * 16)[:T].astype(np.int64)
+    pa.write_kv(k, v, kc, vc, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    KC.write_kv(want_k, want_v, bits(k), bits(v), slots, 16)
+    assert np.array_equal(bits(kc).view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(bits(vc).view(np.uint16), want_v.view(np.uint16))
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_copy_blocks_bit_exact(dtype):
+    g = torch.Generator(device=DEV).manual_seed(2)
+    N, H, D = 30, 8, 128
+    kc = torch.randn(N, H, 16, D, generator=g, device=DEV).to(dtype)
+    vc = torch.randn(N, H, D, 16, generator=g, device=DEV).to(dtype)
+    want_k, want_v = bits(kc), bits(vc)
+    pairs = np.array([[1, 20], [3, 21], [29, 0], [7, 22], [2, 40]], dtype=np.int32)  # last: out of range
+    pa.copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    KC.copy_blocks(want_k, want_v, pairs[:-1])
+    assert np.array_equal(bits(kc).view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(bits(vc).view(np.uint16), want_v.view(np.uint16))
