@@ -3,8 +3,8 @@
 Argument marshalling only: tensors become raw device pointers, the current
 torch stream becomes the hipStream_t, and every step of the hot path runs in
 the library's HIP kernels.  There is no fallback: if libpa.so is missing the
-import fails loudly (build it with ``python -m paged_kv_cache_422_amd.build``
-or ``__graft_entry__.build()``).
+import fails loudly (build it with ``python __graft_entry__.py``, which
+calls ``__graft_entry__.build()``).
 
 Function names and arguments follow include/pa.h.  Cache tensors use the
 library's storage format:
@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libpa.so not found at {LIB_PATH}; build it first "
-                      "(python -m paged_kv_cache_422_amd.build)")
+                      "(python __graft_entry__.py)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_ENOTSUP = range(5)
