@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -58,6 +59,17 @@ pa_status hip_result(const char* fn, hipError_t e) {
   if (e != hipSuccess)
     return fail(PA_EHIP, std::string(fn) + ": " + hipGetErrorString(e));
   return ok();
+}
+
+// Blocks each decode wave keeps in flight.  PA_DECODE_DEPTH (1 or 2)
+// overrides the default for experiments; it is read once per process.
+int32_t decode_depth() {
+  static const int32_t depth = [] {
+    const char* e = std::getenv("PA_DECODE_DEPTH");
+    if (e && (e[0] == '1' || e[0] == '2') && e[1] == '\0') return static_cast<int32_t>(e[0] - '0');
+    return static_cast<int32_t>(2);
+  }();
+  return depth;
 }
 
 int32_t resolve_partition(int32_t requested, int32_t num_q_heads, int32_t num_kv_heads,
@@ -168,8 +180,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t num_sub = (group + 15) / 16;
   const int64_t max_parts = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P);
-  if (static_cast<int64_t>(num_kv_heads) * num_sub > 65535)
-    return fail(PA_ENOTSUP, "pa_decode: too many heads");
+  // One workgroup of 256 work-items per (partition, sequence, head group);
+  // the launch's work-item count must fit the dispatch packet's 32 bits.
+  if (max_parts * num_seqs * num_kv_heads * num_sub * 256 > static_cast<int64_t>(UINT32_MAX))
+    return fail(PA_ENOTSUP, "pa_decode: too many (partition, sequence, head) work items");
   pa::DecodeArgs a{};
   a.out = static_cast<uint16_t*>(out);
   float* ws = static_cast<float*>(workspace);
@@ -191,6 +205,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.part_blocks = P / kBlock;
   a.max_parts = static_cast<int32_t>(max_parts);
   a.max_context_len = max_context_len;
+  a.depth = decode_depth();
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_result(fn, pa::launch_decode(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
 }

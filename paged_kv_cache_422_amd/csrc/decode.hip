@@ -10,16 +10,27 @@
 // GPU Busy"): every K/V byte of the batch is read exactly once per step, so
 // the roofline is HBM and the design goal is to keep enough bytes in flight.
 //
-// Work split (library design, not from the pages): a sequence's context is
-// cut into partitions of part_blocks blocks.  One 256-thread workgroup
-// (4 wave64s) handles one (sequence, KV head, partition) for all query heads
-// of that KV head's group, so K/V are read once per group.  Wave w takes
-// blocks w, w+4, ... of the partition; waves merge through LDS.  A sequence
-// with one partition writes its output directly; otherwise each partition
-// writes (max, sum, unnormalised accumulator) and a second kernel merges them
-// by log-sum-exp.  The order of every reduction depends only on the
-// sequence's own length and the partition size, so the result for a sequence
-// does not depend on the rest of the batch or on where its blocks live.
+// Work split (library design, not from the pages): a sequence of nb blocks
+// is cut into np = ceil(nb / part_blocks) partitions of nearly equal size
+// (partition p covers blocks [p*nb/np, (p+1)*nb/np)), so every work item of a
+// sequence is within one block of the others and long sequences do not leave
+// a short remainder item for the end of the launch.  One 256-thread
+// workgroup (4 wave64s) handles one (sequence, KV head, partition) for all
+// query heads of that KV head's group, so K/V are read once per group.  Wave
+// w takes blocks w, w+4, ... of the partition; waves merge through LDS.  A
+// sequence with one partition writes its output directly; otherwise each
+// partition writes (max, sum, unnormalised accumulator) and a second kernel
+// merges them by log-sum-exp.  The order of every reduction depends only on
+// the sequence's own length and the partition size, so the result for a
+// sequence does not depend on the rest of the batch or on where its blocks
+// live.
+//
+// Launch order: the 1-D grid runs KV head (and query-head sub-group)
+// fastest, then sequence, then partition.  Workgroups are handed to the
+// eight XCDs round-robin by index, so consecutive indices must carry equal
+// work: neighbouring heads of one sequence do, neighbouring partitions of
+// different lengths do not.  Partition-major order also starts every
+// sequence's first partition before any second one.
 //
 // Per 16-token block a wave does (16 = MFMA tile edge = block size):
 //   S^T[16 keys x 16 heads] = K[16 x D] . Q^T[D x 16]    (D/32 MFMA 16x16x32)
@@ -44,8 +55,13 @@ constexpr int kWaves = 4;
 // -1: invalid context length; 0: empty; otherwise number of partitions.
 __device__ __forceinline__ int num_partitions(int L, const DecodeArgs& a) {
   if (L < 0 || L > a.max_context_len || L > a.bt_stride * kBlock) return -1;
-  const int P = a.part_blocks * kBlock;
-  return (L + P - 1) / P;
+  const int nb = (L + kBlock - 1) / kBlock;
+  return (nb + a.part_blocks - 1) / a.part_blocks;
+}
+
+// First block of partition p of a sequence with nb blocks in np partitions.
+__device__ __forceinline__ int partition_start(int p, int nb, int np) {
+  return static_cast<int>(static_cast<int64_t>(p) * nb / np);
 }
 
 template <class T, int D>
@@ -65,18 +81,31 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* k
     r.v[t] = *reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t);
 }
 
-template <class T, int D, int NH>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+// Occupancy target per pipeline depth: DEPTH blocks in flight per wave need
+// (DEPTH + 1) register buffers; depth 1 fits three waves per SIMD, depth 2
+// two.
+template <int DEPTH> struct DecodeOcc;
+template <> struct DecodeOcc<1> { static constexpr int kWavesPerEU = 3; };
+template <> struct DecodeOcc<2> { static constexpr int kWavesPerEU = 2; };
+
+template <class T, int D, int NH, int DEPTH>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(DecodeOcc<DEPTH>::kWavesPerEU, DecodeOcc<DEPTH>::kWavesPerEU)))
+void decode_partition_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int VT = D / 16;
   __shared__ float sm_m[kWaves][NH];
   __shared__ float sm_l[kWaves][NH];
   __shared__ float sm_o[kWaves][NH][D];
 
-  const int part = blockIdx.x;
-  const int s = blockIdx.y;
-  const int g = blockIdx.z / a.num_sub;
-  const int sub = blockIdx.z - g * a.num_sub;
+  // blockIdx.x = (part * num_seqs + s) * (num_kv_heads * num_sub) + head group
+  const int n_hg = a.num_kv_heads * a.num_sub;
+  const int hg = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_hg));
+  const uint32_t rest = blockIdx.x / static_cast<uint32_t>(n_hg);
+  const int s = static_cast<int>(rest % static_cast<uint32_t>(a.num_seqs));
+  const int part = static_cast<int>(rest / static_cast<uint32_t>(a.num_seqs));
+  const int g = hg / a.num_sub;
+  const int sub = hg - g * a.num_sub;
   const int hq0 = g * a.group + sub * 16;
   const int nh = min(16, a.group - sub * 16);
   const int tid = threadIdx.x;
@@ -98,8 +127,9 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   }
   if (part >= np) return;
 
-  const int blk0 = part * a.part_blocks;
-  const int nblk = min(a.part_blocks, (L + kBlock - 1) / kBlock - blk0);
+  const int nb_seq = (L + kBlock - 1) / kBlock;
+  const int blk0 = partition_start(part, nb_seq, np);
+  const int nblk = partition_start(part + 1, nb_seq, np) - blk0;   // 1 .. part_blocks
 
   // This partition's block ids, one per lane (part_blocks <= 64).
   int my_bt = 0;
@@ -131,13 +161,8 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  BlockRegs<T, D> cur, nxt;
-  int j = w;
-  if (j < nblk) load_block<T, D>(cur, kbase, vbase, __builtin_amdgcn_readlane(my_bt, j) * blk_elems);
-  for (; j < nblk; j += kWaves) {
-    const int jn = j + kWaves;
-    if (jn < nblk) load_block<T, D>(nxt, kbase, vbase, __builtin_amdgcn_readlane(my_bt, jn) * blk_elems);
-
+  // One 16-token block: scores, online-softmax update, P.V accumulate.
+  auto process = [&](BlockRegs<T, D>& cur, int j) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sacc = mfma16x16x32<T>(cur.k[ks], qb[ks], sacc);
@@ -200,7 +225,52 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
       if constexpr (SplitP<T>::kSplit) c = mfma16x16x16<T>(pal, cur.v[t], c);
       o[t] = c;
     }
-    cur = nxt;
+  };
+
+  // Software pipeline over DEPTH + 1 register buffers: the loads of the
+  // next DEPTH blocks a wave handles are in flight while it works on the
+  // current one.  Prefetches are issued unconditionally (past the end they
+  // re-read the wave's last block, which the cache still holds) so that the
+  // wait before each block only covers that block's own loads.
+  auto blk_off = [&](int jj) {
+    return static_cast<int64_t>(__builtin_amdgcn_readlane(my_bt, jj)) * blk_elems;
+  };
+  int j = w;
+  const int j_last = w + ((nblk - 1 - w) / kWaves) * kWaves;   // this wave's last block
+  auto nxt = [&](int jj) { return jj < nblk ? jj : j_last; };
+  if (j < nblk) {
+    if constexpr (DEPTH == 1) {
+      BlockRegs<T, D> b0, b1;
+      load_block<T, D>(b0, kbase, vbase, blk_off(j));
+      for (;;) {
+        load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + kWaves)));
+        process(b0, j);
+        j += kWaves;
+        if (j >= nblk) break;
+        load_block<T, D>(b0, kbase, vbase, blk_off(nxt(j + kWaves)));
+        process(b1, j);
+        j += kWaves;
+        if (j >= nblk) break;
+      }
+    } else {
+      BlockRegs<T, D> b0, b1, b2;
+      load_block<T, D>(b0, kbase, vbase, blk_off(j));
+      load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + kWaves)));
+      for (;;) {
+        load_block<T, D>(b2, kbase, vbase, blk_off(nxt(j + 2 * kWaves)));
+        process(b0, j);
+        j += kWaves;
+        if (j >= nblk) break;
+        load_block<T, D>(b0, kbase, vbase, blk_off(nxt(j + 2 * kWaves)));
+        process(b1, j);
+        j += kWaves;
+        if (j >= nblk) break;
+        load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + 2 * kWaves)));
+        process(b2, j);
+        j += kWaves;
+        if (j >= nblk) break;
+      }
+    }
   }
 
   // Per-head sums over the four key groups of the wave.
@@ -292,8 +362,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 template <class T, int D, int NH>
 hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.max_parts, a.num_seqs, a.num_kv_heads * a.num_sub);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, NH>), grid, dim3(256), 0, stream, a);
+  const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
+  if (a.depth == 1)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 1>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 2>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;

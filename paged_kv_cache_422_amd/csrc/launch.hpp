@@ -48,6 +48,7 @@ struct DecodeArgs {
   int32_t part_blocks;        // partition size in blocks
   int32_t max_parts;
   int32_t max_context_len;
+  int32_t depth;              // blocks in flight per wave (1 or 2)
   float scale_log2;           // scale * log2(e)
 };
 
