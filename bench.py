@@ -1,26 +1,34 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-Default workload: LLaMA-7B-shaped paged decode, 64 sequences, 32 heads MHA,
-head_dim 128, fp16, context lengths U[128, 2048], 16-token blocks scattered
-through a pool of 1.2x demand.  A step is one pa_decode call (partition
-kernel + log-sum-exp merge kernel) over the whole batch; inputs are resident
-in HBM before timing starts.
+Default workload (the headline): LLaMA-7B-shaped paged decode, 64 sequences,
+32 heads MHA, head_dim 128, fp16, context lengths U[128, 2048], 16-token
+blocks scattered through a pool of 1.2x demand.  A step is one pa_decode call
+over the whole batch; inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line: KV GB/s (algorithmic bytes: sum_s L_s * 2 * Hkv * D * 2
-per step, divided by the measured step time), us/step, the roofline of the
+Timing protocol: W untimed warm-up steps, then K timed steps.  Before every
+step (outside its timed region) a 512 MiB buffer is read, which evicts the
+256 MB Infinity Cache, so each step reads its K/V from HBM as a decode step
+in a real model would (the layers in between stream their weights through
+the cache).  Each step is bracketed by HIP events on the stream the kernels
+run on; ms_per_step is their mean.  --warm-cache drops the eviction.
+
+Prints ONE JSON line: KV GB/s (algorithmic bytes: sum_s L_s * 2 * Hkv * D *
+2 per step, divided by the measured step time), us/step, the roofline of the
 dominant kernel, and the fp64 CPU oracle timed on a bounded sample of the
 same workload on this host's cores.
 
-Other workloads (--workload): llama8b_gqa, llama13b_shared (not for the
-headline), mixed (write + 2 prefill chunks + 4096 decode), tiny.
+Other workloads (--workload): llama8b_gqa, llama13b_shared (prefix sharing
+built through the block pool), mixed (slot-mapped write + 2 prefill chunks +
+4096 decode sequences, each call timed), tiny.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
-import resource
+import re
 import sys
 import time
 
@@ -28,8 +36,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+MFMA_16BIT_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+METRIC = "paged-decode KV GB/s (% of HBM peak) + \u00b5s/step, batch 64 LLaMA-7B shape"
+FLUSH_BYTES = 512 << 20
+DECODE_SOURCES = ("paged_kv_cache_422_amd/csrc/decode.hip", "paged_kv_cache_422_amd/csrc/common.hpp")
 
 
 def parse():
@@ -43,91 +54,163 @@ def parse():
                     help="partition size in tokens (-1: the workload's own, 0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline sample (0: skip)")
+    ap.add_argument("--warm-cache", action="store_true",
+                    help="do not evict the Infinity Cache between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device copies of 1 GiB (torch's copy kernel), the known-size "
+                         "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
 
 
-class Timer:
-    """HIP events on the stream the kernels run on (torch's current stream)."""
+def copy_calibration(torch):
+    """Five copies of 1 GiB: each reads and writes exactly 2^30 bytes."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 1 << 30, "copy_calibration_bytes_written": 1 << 30,
+                      "launches": 5}), flush=True)
+    return 0
 
-    def __init__(self, torch):
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(name: str, paths):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_h = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != source_digest(paths):
+        return None
+    return int(m_b.group(1))
+
+
+class StepTimer:
+    """Per-step HIP events on the current stream, with an optional cache
+    eviction (a full read of a 512 MiB buffer) before each step."""
+
+    def __init__(self, torch, evict: bool):
         self.torch = torch
-        self.pairs = []
+        self.junk = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if evict else None
 
-    def __call__(self, fn):
+    def evict(self):
+        if self.junk is not None:
+            self.junk.sum()
+
+    def run(self, steps, fns):
+        """fns: list of callables forming one step; returns per-call ms lists."""
         t = self.torch
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pairs.append((a, b))
+        ev = [[t.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        t.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in ev:
+            self.evict()
+            e[0].record()
+            for i, fn in enumerate(fns):
+                fn()
+                e[i + 1].record()
+        t.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        per = [[e[i].elapsed_time(e[i + 1]) for e in ev] for i in range(len(fns))]
+        total = [e[0].elapsed_time(e[-1]) for e in ev]
+        return per, total, wall
 
-    def mean_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(len(self.pairs), 1)
+
+def mean(xs):
+    return sum(xs) / max(len(xs), 1)
 
 
-def cpu_oracle_sample(w, q, kc, vc, budget_s):
-    """fp64 oracle over the workload's sequences in order (wrapping around for
-    further passes) until the time budget is spent.  Returns (GB/s of KV
-    processed, sequences done, wall seconds, cores used)."""
+def median(xs):
+    s = sorted(xs)
+    return s[len(s) // 2] if s else 0.0
+
+
+def bits(t):
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    return t.numpy() if t.dtype == torch.float16 else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_oracle_decode(q, kc, vc, block_tables, context_lens, scale, dtype, budget_s, seqs=None):
+    """fp64 oracle over sequences in order (wrapping around) until the time
+    budget is spent.  Device -> host copies are not timed.  Returns (KV GB/s
+    processed, sequences done, wall seconds, threads used)."""
     import numpy as np
     import torch
     from oracle import attention as A
 
-    def bits(t):
-        t = t.detach().cpu().contiguous()
-        return t.numpy() if t.dtype == torch.float16 else t.view(torch.int16).numpy().view(np.uint16)
-
-    # Copy back each sequence's blocks once (device -> host is not timed).
-    per_seq = []
+    order = list(range(len(context_lens))) if seqs is None else list(seqs)
+    per_seq = {}
     qh = bits(q)
-    for s in range(w.num_seqs):
-        L = int(w.context_lens[s])
-        nb = -(-L // 16)
-        it = torch.from_numpy(w.block_tables[s, :nb].astype(np.int64)).to(kc.device)
-        per_seq.append((L, bits(kc[it]), bits(vc[it]), np.arange(nb, dtype=np.int32)[None]))
-    t0, c0 = time.perf_counter(), time.process_time()
-    done = bytes_done = 0
-    while True:
-        s = done % w.num_seqs
-        L, kh, vh, bt = per_seq[s]
-        A.decode(qh[s:s + 1], kh, vh, bt, [L], w.scale, w.dtype)
-        bytes_done += L * 2 * w.num_kv_heads * w.head_dim * 2
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
-    cores = max(1, round(cpu / wall)) if wall > 0 else 1
-    return bytes_done / wall / 1e9, done, wall, cores
-
-
-def bench_decode(args, torch, pa, w):
-    dev = "cuda"
-    q, kc, vc = w.make_tensors(dev)
-    bt = torch.from_numpy(w.block_tables).to(dev)
-    ctx = torch.from_numpy(w.context_lens).to(dev)
-    P = w.partition_size if args.partition < 0 else args.partition
-    need = pa.decode_workspace_size(w.num_seqs, w.num_q_heads, w.head_dim, w.max_model_len, P,
-                                    w.num_kv_heads)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-
-    def step():
-        pa.decode(out, q, kc, vc, bt, ctx, w.max_model_len, w.scale, P, ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timer = Timer(torch)
+    Hkv, D = kc.shape[1], kc.shape[-1]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        timer(step)
+    c0 = time.process_time()
+    done = bytes_done = 0
+    spent = 0.0
+    while spent < budget_s:
+        s = order[done % len(order)]
+        if s not in per_seq:
+            L = int(context_lens[s])
+            nb = -(-L // 16)
+            idx = torch.from_numpy(block_tables[s, :nb].astype(np.int64)).to(kc.device)
+            pause = time.perf_counter()
+            per_seq[s] = (L, bits(kc[idx]), bits(vc[idx]), np.arange(nb, dtype=np.int32)[None])
+            t0 += time.perf_counter() - pause          # copy-back is not oracle work
+        L, kh, vh, bt = per_seq[s]
+        A.decode(qh[s:s + 1], kh, vh, bt, [L], scale, dtype)
+        bytes_done += L * 2 * Hkv * D * 2
+        done += 1
+        spent = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    threads = max(1, round(cpu / spent)) if spent > 0 else 1
+    return bytes_done / spent / 1e9, done, spent, threads
+
+
+def build_shared_cache(torch, pa, w, k_tok, v_tok):
+    """Lay the prefix-sharing workload out through the block pool: each
+    group's prompt is appended once, forked to the other members, then every
+    member appends its own tokens (copy-on-write for the shared partial
+    block)."""
+    pool = pa.BlockPool(w.num_blocks, 16, 7)
+    H, D = w.num_kv_heads, w.head_dim
+    kc = torch.zeros((w.num_blocks, H, 16, D), dtype=k_tok.dtype, device="cuda")
+    vc = torch.zeros((w.num_blocks, H, D, 16), dtype=k_tok.dtype, device="cuda")
+    seqs = [None] * w.num_seqs
+
+    def write(i, sid, lo, hi):
+        slots, cow = pool.append(sid, hi - lo)
+        if cow:
+            pa.copy_blocks(kc, vc, torch.tensor(cow, dtype=torch.int32, device="cuda"))
+        rows = torch.from_numpy(w.token_rows[i][lo:hi]).cuda()
+        pa.write_kv(k_tok[rows], v_tok[rows], kc, vc, torch.tensor(slots, dtype=torch.int64, device="cuda"))
+
+    G = w.group_size
+    for k in range(w.num_seqs // G):
+        P = int(w.prefix_lens[k])
+        members = list(range(k * G, (k + 1) * G))
+        root = pool.create()
+        write(members[0], root, 0, P)
+        seqs[members[0]] = root
+        for s in members[1:]:
+            seqs[s] = pool.fork(root)
+        for s in members:
+            write(s, seqs[s], P, int(w.context_lens[s]))
+    bt, ctx = pool.block_tables(seqs, w.bt_stride, pad=0)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms = timer.mean_ms()
-    kv = w.kv_bytes
-    gbs = kv / (ms * 1e-3) / 1e9
-    return dict(ms=ms, wall_ms=wall_ms, gbs=gbs, kv=kv, q=q, kc=kc, vc=vc, P=P)
+    used = pool.num_blocks - pool.num_free
+    return kc, vc, bt, ctx, used
 
 
 def main():
@@ -135,7 +218,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by sequence or KV head with no exchange inside attention, "
-              "but multi-GPU runs are not part of it.", file=sys.stderr)
+              "but runs on more than one GPU are not part of it.", file=sys.stderr)
         return 2
     import numpy as np
     import torch
@@ -146,52 +229,124 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        return copy_calibration(torch)
     name = args.workload
     w = W.make_workload(name)
+    timer = StepTimer(torch, evict=not args.warm_cache)
+    extra = {}
+
     if name == "mixed":
-        raise SystemExit("use --workload mixed via bench_mixed (not in this build yet)")
-    if name == "llama13b_shared":
-        raise SystemExit("llama13b_shared is benchmarked through the tests' pool layout")
-    r = bench_decode(args, torch, pa, w)
+        kc, vc, k_new, v_new, q_dec, q_pre = w.make_tensors("cuda")
+        sm = torch.from_numpy(w.slot_mapping).cuda()
+        pbt = torch.from_numpy(w.prefill_bt).cuda()
+        qsl = torch.from_numpy(w.q_start_loc).cuda()
+        psl = torch.from_numpy(w.prefill_seq_lens).cuda()
+        dbt = torch.from_numpy(w.decode_bt).cuda()
+        dctx = torch.from_numpy(w.decode_lens).cuda()
+        P = w.partition_size if args.partition < 0 else args.partition
+        ws = torch.empty(max(pa.decode_workspace_size(w.num_decode, w.num_q_heads, w.head_dim,
+                                                      w.max_model_len, P, w.num_kv_heads), 1),
+                         dtype=torch.uint8, device="cuda")
+        out_pre, out_dec = torch.empty_like(q_pre), torch.empty_like(q_dec)
+        fns = [lambda: pa.write_kv(k_new, v_new, kc, vc, sm),
+               lambda: pa.prefill_chunk(out_pre, q_pre, kc, vc, pbt, qsl, psl, w.prefill_chunk,
+                                        w.prefill_cached + w.prefill_chunk, w.scale),
+               lambda: pa.decode(out_dec, q_dec, kc, vc, dbt, dctx, w.max_model_len, w.scale, P, ws)]
+        kv_bytes = w.decode_kv_bytes
+        q_dec_t, kc_t, vc_t, bt_np, ctx_np = q_dec, kc, vc, w.decode_bt, w.decode_lens
+        num_seqs, Hq, Hkv, D = w.num_decode, w.num_q_heads, w.num_kv_heads, w.head_dim
+    else:
+        if name == "llama13b_shared":
+            q, k_tok, v_tok = w.make_tensors("cuda")
+            kc, vc, bt_np, ctx_np, used = build_shared_cache(torch, pa, w, k_tok, v_tok)
+            del k_tok, v_tok
+            P = 0 if args.partition < 0 else args.partition
+            extra["unique_kv_bytes_per_step"] = w.unique_kv_bytes
+            extra["pool_blocks_used"] = int(used)
+        else:
+            q, kc, vc = w.make_tensors("cuda")
+            bt_np, ctx_np = w.block_tables, w.context_lens
+            P = w.partition_size if args.partition < 0 else args.partition
+        bt = torch.from_numpy(bt_np).cuda()
+        ctx = torch.from_numpy(ctx_np).cuda()
+        ws = torch.empty(max(pa.decode_workspace_size(w.num_seqs, w.num_q_heads, w.head_dim,
+                                                      w.max_model_len, P, w.num_kv_heads), 1),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        fns = [lambda: pa.decode(out, q, kc, vc, bt, ctx, w.max_model_len, w.scale, P, ws)]
+        kv_bytes = w.kv_bytes
+        q_dec_t, kc_t, vc_t = q, kc, vc
+        num_seqs, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+
+    timer.run(args.warmup, fns)
+    per, total, wall = timer.run(args.steps, fns)
+    ms = mean(total)
+    dec_ms = mean(per[-1])                       # pa_decode is the last call of every step
+    gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+
+    if name == "mixed":
+        w_ms, p_ms = mean(per[0]), mean(per[1])
+        extra["calls_us"] = {"write_kv": round(w_ms * 1e3, 2), "prefill_chunk": round(p_ms * 1e3, 2),
+                             "decode": round(dec_ms * 1e3, 2)}
+        extra["write_kv"] = {"bytes": w.write_bytes, "GB/s": round(w.write_bytes / (w_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(w.write_bytes / (w_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        tflops = w.prefill_flops / (p_ms * 1e-3) / 1e12
+        extra["prefill_chunk"] = {"flop": w.prefill_flops, "TFLOP/s": round(tflops, 1),
+                                  "frac_mfma": round(tflops / MFMA_16BIT_PEAK_TFLOPS, 4)}
+
     cpu = None
     if args.cpu_budget > 0:
-        gbs_cpu, n_seq, wall, cores = cpu_oracle_sample(w, r["q"], r["kc"], r["vc"], args.cpu_budget)
-        cpu = {"value": round(gbs_cpu, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"{n_seq} sequence decodes (all heads; the workload's {w.num_seqs} "
-                         f"sequences in order, repeated) in {wall:.1f} s, fp64 numpy"}
+        seqs = None
+        if name == "mixed":
+            rng = np.random.default_rng(5)
+            seqs = sorted(rng.choice(num_seqs, 64, replace=False).tolist())
+        gbs_cpu, n_seq, wall_cpu, threads = cpu_oracle_decode(
+            q_dec_t, kc_t, vc_t, bt_np, ctx_np, w.scale, w.dtype, args.cpu_budget, seqs)
+        cpu = {"value": round(gbs_cpu, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n_seq} single-sequence fp64 decodes (all {Hq} query heads each) over "
+                         f"{'a seeded 64-sequence subset' if seqs else f'the {num_seqs} sequences'} "
+                         f"of this workload in order, in {wall_cpu:.1f} s; KV GB/s of the sample"}
+
+    traffic = profiled_traffic(f"decode_{name}_pmc.md", DECODE_SOURCES)
     line = {
-        "metric": "paged-decode KV GB/s (% of HBM peak) + us/step, batch 64 LLaMA-7B shape",
-        "value": round(r["gbs"], 2),
+        "metric": METRIC,
+        "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms"], 5),
-        "us_per_step": round(r["ms"] * 1e3, 2),
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_median": round(median(total) * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"{name} paged decode: {w.num_seqs} seqs, {w.num_q_heads} q heads / "
-                        f"{w.num_kv_heads} kv heads, D {w.head_dim}, block 16, {w.dtype}",
-            "num_seqs": w.num_seqs,
-            "kv_bytes_per_step": r["kv"],
-            "partition_size": r["P"] or pa.default_partition_size(w.num_q_heads, w.num_kv_heads, w.head_dim),
+            "workload": f"{name}: paged decode of {num_seqs} sequences, {Hq} query heads over {Hkv} "
+                        f"KV heads, head_dim {D}, 16-token blocks, {w.dtype}"
+                        + (" (plus slot-mapped write of 8192 tokens and 2 prefill chunks of 2048)"
+                           if name == "mixed" else ""),
+            "num_seqs": num_seqs,
+            "kv_bytes_per_step": int(kv_bytes),
+            "partition_size": P or pa.default_partition_size(Hq, Hkv, D),
+            "cache": "warm" if args.warm_cache else "Infinity Cache evicted before each step",
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(r["gbs"], 2),
+            "achieved": round(gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "pa_decode step (decode_partition_kernel + decode_merge_kernel)",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "pa_decode (partition kernel + log-sum-exp merge kernel)",
         },
         "cpu_baseline": cpu,
-        "wall_ms_per_step": round(r["wall_ms"], 5),
+        "wall_ms_per_step": round(wall, 5),
+        **extra,
     }
     print(json.dumps(line), flush=True)
     return 0
