@@ -115,7 +115,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
  *   partition_size  long contexts are cut into partitions of this many
  *                   tokens, each handled by its own workgroup, and merged by
  *                   log-sum-exp in a second kernel.  0 = library default
- *                   (pa_default_partition_size).  Multiple of 16, <= 1024.
+ *                   (pa_default_partition_size).  Multiple of 16, <= 4096.
  *                   The result for a sequence depends only on its own data
  *                   and on the partition size, never on the rest of the batch.
  *   workspace       device scratch of at least pa_decode_workspace_size()

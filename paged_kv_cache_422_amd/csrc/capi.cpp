@@ -38,7 +38,7 @@ pa_status ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kBlock = 16;
-constexpr int kMaxPartitionTokens = 1024;   // one block id per lane of a wave64
+constexpr int kMaxPartitionTokens = 4096;   // 4 block ids per lane of a wave64
 
 pa_status check_common(const char* fn, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        pa_dtype dtype) {
@@ -123,11 +123,17 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, const
   return hip_result(fn, pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
+// Every partition beyond a sequence's first writes a partial state (head_dim
+// + 2 floats per query head) that the second pass reads back.  On MI355X those
+// writes cost about ten times their size in lost read bandwidth, so the
+// default keeps partitions long: 1024 tokens (64 blocks, 16 per wave) still
+// leaves several workgroups per (sequence, KV head) for contexts of a few
+// thousand tokens while halving the partial traffic of 512.
 int32_t pa_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
   (void)num_q_heads;
   (void)num_kv_heads;
   (void)head_dim;
-  return 512;
+  return 1024;
 }
 
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -162,7 +168,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return fail(PA_EINVAL, "pa_decode: num_q_heads must be a positive multiple of num_kv_heads");
   if (partition_size != 0 &&
       (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > kMaxPartitionTokens))
-    return fail(PA_ENOTSUP, "pa_decode: partition_size must be 0 or a multiple of 16 in [16, 1024]");
+    return fail(PA_ENOTSUP, "pa_decode: partition_size must be 0 or a multiple of 16 in [16, 4096]");
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_EINVAL, "pa_decode: null pointer");

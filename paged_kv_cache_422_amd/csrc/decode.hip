@@ -51,6 +51,7 @@ namespace {
 
 constexpr int kBlock = 16;   // tokens per KV block == MFMA tile edge
 constexpr int kWaves = 4;
+constexpr int kBtRegs = 4;   // block-table registers per lane: partitions up to 256 blocks
 
 // -1: invalid context length; 0: empty; otherwise number of partitions.
 __device__ __forceinline__ int num_partitions(int L, const DecodeArgs& a) {
@@ -131,12 +132,23 @@ void decode_partition_kernel(DecodeArgs a) {
   const int blk0 = partition_start(part, nb_seq, np);
   const int nblk = partition_start(part + 1, nb_seq, np) - blk0;   // 1 .. part_blocks
 
-  // This partition's block ids, one per lane (part_blocks <= 64).
-  int my_bt = 0;
-  if (lane < nblk) my_bt = a.block_tables[static_cast<int64_t>(s) * a.bt_stride + blk0 + lane];
-  const bool bad_id = lane < nblk && (my_bt < 0 || my_bt >= a.num_blocks);
+  // This partition's block ids, 64 per register with one per lane
+  // (part_blocks <= 64 * kBtRegs).
+  int my_bt[kBtRegs];
+  bool bad_id = false;
+  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(s) * a.bt_stride + blk0;
+#pragma unroll
+  for (int r = 0; r < kBtRegs; ++r) {
+    my_bt[r] = 0;
+    if (64 * r < nblk) {                      // wave-uniform
+      const int jj = 64 * r + lane;
+      if (jj < nblk) my_bt[r] = bt_row[jj];
+      const bool bad = jj < nblk && (my_bt[r] < 0 || my_bt[r] >= a.num_blocks);
+      bad_id |= bad;
+      if (bad) my_bt[r] = 0;
+    }
+  }
   const bool poison = __any(bad_id);
-  if (bad_id) my_bt = 0;
 
   // Q^T operand: head column hl, dims 32*ks + 8*quad .. +7 (zero padding
   // columns beyond the group).
@@ -233,7 +245,12 @@ void decode_partition_kernel(DecodeArgs a) {
   // re-read the wave's last block, which the cache still holds) so that the
   // wait before each block only covers that block's own loads.
   auto blk_off = [&](int jj) {
-    return static_cast<int64_t>(__builtin_amdgcn_readlane(my_bt, jj)) * blk_elems;
+    const int r = jj >> 6;                    // wave-uniform
+    int id = __builtin_amdgcn_readlane(my_bt[0], jj & 63);
+#pragma unroll
+    for (int k = 1; k < kBtRegs; ++k)
+      if (r == k) id = __builtin_amdgcn_readlane(my_bt[k], jj & 63);
+    return static_cast<int64_t>(id) * blk_elems;
   };
   int j = w;
   const int j_last = w + ((nblk - 1 - w) / kWaves) * kWaves;   // this wave's last block

@@ -41,7 +41,7 @@ def test_version():
     (dict(dtype=7), pa.PA_ENOTSUP),
     (dict(num_q_heads=33), pa.PA_EINVAL),
     (dict(partition_size=40), pa.PA_ENOTSUP),
-    (dict(partition_size=2048), pa.PA_ENOTSUP),
+    (dict(partition_size=8192), pa.PA_ENOTSUP),
     (dict(num_seqs=-1), pa.PA_EINVAL),
     (dict(bt_stride=0), pa.PA_EINVAL),
     (dict(), pa.PA_EINVAL),                         # null pointers

@@ -144,8 +144,18 @@ def test_partition_size_changes_only_rounding():
     lens = [2000, 1500, 999]
     q, kc, vc, bt, ctx = small_case(3, 8, 8, 128, torch.float16, lens, seed=14)
     want = oracle_decode(q, kc, vc, bt, ctx, 0.088)
-    for P in (16, 128, 512, 1024):
+    for P in (16, 128, 512, 1024, 2048):
         assert_close(run_decode(q, kc, vc, bt, ctx, 2048, 0.088, P), want, what=f"P={P}")
+
+
+def test_long_partitions_use_every_table_register():
+    """Partitions of 1040..4096 tokens read block ids from all four per-lane
+    table registers (64 blocks each), including a partial last register."""
+    lens = [4096, 3000, 1041, 65 * 16, 64 * 16 + 1]
+    q, kc, vc, bt, ctx = small_case(len(lens), 8, 2, 128, torch.bfloat16, lens, seed=15)
+    want = oracle_decode(q, kc, vc, bt, ctx, 0.088)
+    for P in (4096, 2048, 1040):
+        assert_close(run_decode(q, kc, vc, bt, ctx, 4096, 0.088, P), want, what=f"P={P}")
 
 
 @pytest.mark.parametrize("make", [llama7b, llama8b_gqa], ids=["llama7b", "llama8b_gqa"])

@@ -219,7 +219,7 @@ class MixedWorkload:
     slot_mapping: np.ndarray         # int64 [T]: decode tokens, then chunks
     num_blocks: int
     pad_block: int
-    partition_size: int = 512
+    partition_size: int = 0           # 0: library default
     max_model_len: int = 4096
     block_size: int = BLOCK_SIZE
 
