@@ -20,7 +20,9 @@ same workload on this host's cores.
 
 Other workloads (--workload): llama8b_gqa, llama13b_shared (prefix sharing
 built through the block pool), mixed (slot-mapped write + 2 prefill chunks +
-4096 decode sequences, each call timed), tiny.
+4096 decode sequences, each call timed), tiny, and prefill (the mixed step's
+slot-mapped write and two 2048-row chunks alone, without its decode batch:
+the MFMA-bound part, reported against the matrix-core roofline).
 """
 from __future__ import annotations
 
@@ -49,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny"])
+                    choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's own, 0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -232,9 +234,44 @@ def main():
     if args.copy_calibration:
         return copy_calibration(torch)
     name = args.workload
-    w = W.make_workload(name)
+    w = W.mixed(num_decode=0) if name == "prefill" else W.make_workload(name)
     timer = StepTimer(torch, evict=not args.warm_cache)
     extra = {}
+
+    if name == "prefill":
+        kc, vc, k_new, v_new, q_dec, q_pre = w.make_tensors("cuda")
+        sm = torch.from_numpy(w.slot_mapping).cuda()
+        pbt = torch.from_numpy(w.prefill_bt).cuda()
+        qsl = torch.from_numpy(w.q_start_loc).cuda()
+        psl = torch.from_numpy(w.prefill_seq_lens).cuda()
+        out_pre = torch.empty_like(q_pre)
+        pa.write_kv(k_new, v_new, kc, vc, sm)
+        fns = [lambda: pa.prefill_chunk(out_pre, q_pre, kc, vc, pbt, qsl, psl, w.prefill_chunk,
+                                        w.prefill_cached + w.prefill_chunk, w.scale)]
+        timer.run(args.warmup, fns)
+        per, total, wall = timer.run(args.steps, fns)
+        ms = mean(total)
+        tflops = w.prefill_flops / (ms * 1e-3) / 1e12
+        line = {
+            "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "us_per_step": round(ms * 1e3, 2), "us_per_step_median": round(median(total) * 1e3, 2),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic",
+            "config": {"workload": f"prefill: {w.num_chunks} chunks of {w.prefill_chunk} query rows over "
+                                   f"{w.prefill_cached} cached tokens, {w.num_q_heads} query heads over "
+                                   f"{w.num_kv_heads} KV heads, head_dim {w.head_dim}, {w.dtype}",
+                       "flop_per_step": int(w.prefill_flops),
+                       "cache": "warm" if args.warm_cache else "Infinity Cache evicted before each step",
+                       "parallelism": "none (1 GPU)"},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_16BIT_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_16BIT_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "pa_prefill_chunk (prefill_kernel)"},
+            "cpu_baseline": None,
+            "wall_ms_per_step": round(wall, 5),
+        }
+        print(json.dumps(line), flush=True)
+        return 0
 
     if name == "mixed":
         kc, vc, k_new, v_new, q_dec, q_pre = w.make_tensors("cuda")

@@ -12,18 +12,27 @@
 //
 // This is a dense contraction, so it runs on the matrix cores (MFMA
 // 32x32x16, fp32 accumulate).  Flash-style tiling:
-//   one wave64  = 32 query rows of one query head,
-//   one 256-thread workgroup = 4 waves over (heads of one KV group) x (row
-//   tiles), so the 4 waves read the same K/V tiles (L1/L2 reuse),
-//   key tiles of 32 = two 16-token blocks.
-// Per key tile a wave computes S^T[32 keys x 32 rows] = K . Q^T (D/16 MFMAs),
-// masks the causal diagonal and the sequence end, updates an online softmax
-// per row in registers, and accumulates O^T[D x 32 rows] += V^T . P^T
-// (2 * D/32 MFMAs).  The accumulator layout of S^T is the operand layout P^T
-// needs (keys permuted consistently in V^T), and O^T's columns are the same
-// rows as S^T's, so neither probabilities nor rescale factors move between
-// lanes.  V is stored dim-major per block, so V^T operands are 8-byte loads.
-// Row tiles are dispatched heaviest (longest causal range) first.
+//   one wave64 = 32 query rows of one query head;
+//   one 512-thread workgroup = 8 waves over (heads of one KV group) x (row
+//   tiles), all reading the same keys;
+//   key tiles of 64 keys (four 16-token blocks) are staged in LDS once per
+//   workgroup: the K/V of the next two tiles are in flight in registers
+//   while the current tile is computed, then written to LDS between two
+//   barriers.
+// Per key tile a wave computes S^T[64 keys x 32 rows] = K . Q^T (two 32-key
+// halves, D/16 MFMAs each), masks the causal diagonal and the sequence end,
+// updates an online softmax per row in registers, and accumulates
+// O^T[D x 32 rows] += V^T . P^T (D/32 x 4 MFMAs).
+//
+// Operand layouts.  In LDS the K rows of each 32-key half are stored with
+// bits 2 and 3 of the key index swapped, so the accumulator element i of
+// lane l (half h = l / 32) holds key 16 * (i / 8) + 8 * h + i % 8: the eight
+// probabilities a lane feeds to the P.V step for 16 keys are its own eight
+// consecutive accumulator elements, and the matching V^T operand is eight
+// consecutive keys of one dimension, i.e. 16 contiguous bytes of the
+// dim-major V block.  LDS rows are padded by 16 bytes so that the 16-byte
+// operand reads of a wave hit distinct banks.  Row tiles are dispatched
+// heaviest (longest causal range) first.
 #include <math.h>
 
 #include "common.hpp"
@@ -34,22 +43,47 @@ namespace pa {
 namespace {
 
 constexpr int kBlock = 16;
+constexpr int kTileKeys = 64;                      // keys per LDS stage
+constexpr int kTileBlocks = kTileKeys / kBlock;
+
+template <int D>
+struct PrefillLds {
+  static constexpr int kRow = D * 2 + 16;          // bytes per K row (one key)
+  static constexpr int kVRow = kBlock * 2 + 16;    // bytes per V row (one dim of a block)
+  static constexpr int kBytesK = kTileKeys * kRow;
+  static constexpr int kBytesVBlock = D * kVRow;
+  static constexpr int kBytes = kBytesK + kTileBlocks * kBytesVBlock;
+};
+
+// Position of key r (0..31) of a 32-key half in LDS: bits 2 and 3 swapped.
+__device__ __forceinline__ int swap_bits23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
 template <class T, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-  constexpr int KS = D / 16;   // QK k-steps
-  constexpr int DT = D / 32;   // 32-dim output tiles
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillArgs a) {
+  using Lds = PrefillLds<D>;
+  constexpr int KS = D / 16;                 // QK^T k-steps
+  constexpr int DT = D / 32;                 // 32-dim output tiles
+  constexpr int UPB = 2 * D;                 // 16-byte units per block per tensor
+  constexpr int UPT = kTileBlocks * UPB / kPrefillThreads;   // units per thread per tensor per tile
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Lds::kBytes];
+
   const int c = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;          // 0 / 1: which 8-element k slice / key group
+  const int half = lane >> 5;
   const int r32 = lane & 31;
 
   // Waves split over heads of the group first, then over row tiles.
   const int G = a.group;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int tiles_per_wg = 4 / hpw;
+  const int tiles_per_wg = kPrefillWaves / hpw;
   const int nhsub = G / hpw;
   const int g = blockIdx.z / nhsub;
   const int hsub = blockIdx.z - g * nhsub;
@@ -63,9 +97,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int n = a.q_start_loc[c + 1] - r_start;
   const int L = a.seq_lens[c];
   const int n_cached = L - n;
-  if (n <= 0 || n > a.max_q_len) return;   // nothing addressable to write
-  const int row0 = rb * wg_rows + rt * 32;
-  if (row0 >= n) return;
+  if (n <= 0 || n > a.max_q_len) return;     // nothing addressable to write
+  const int wg_row0 = rb * wg_rows;
+  if (wg_row0 >= n) return;                  // whole workgroup past the chunk
+  const int row0 = wg_row0 + rt * 32;
+  const bool wave_on = row0 < n;
   const int my_row = row0 + r32;
   const bool row_ok = my_row < n;
   const int64_t out_row = (static_cast<int64_t>(r_start) + my_row) * a.num_q_heads + hq;
@@ -90,15 +126,76 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < KS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
   }
 
-  const int last_row = min(row0 + 31, n - 1);
-  const int key_end = n_cached + last_row + 1;       // keys this wave needs
-  const int n_tiles = (key_end + 31) / 32;
+  const int wg_last_row = min(wg_row0 + wg_rows - 1, n - 1);
+  const int key_end = n_cached + wg_last_row + 1;            // keys the workgroup needs
+  const int n_tiles = __builtin_amdgcn_readfirstlane((key_end + kTileKeys - 1) / kTileKeys);
   const int nb_seq = (L + kBlock - 1) / kBlock;
-  const int lim = min(n_cached + my_row, L - 1);      // last visible key of my row
+  const int lim = min(n_cached + my_row, L - 1);              // last visible key of my row
+  const int wave_lim = min(n_cached + min(row0 + 31, n - 1), L - 1);    // last key any row of the wave sees
+  const int wave_lim_lo = min(n_cached + row0, L - 1);                  // last key every row of the wave sees
   const int32_t* bt = a.block_tables + static_cast<int64_t>(c) * a.bt_stride;
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
   const int64_t head_off = static_cast<int64_t>(g) * tile_elems;
+
+  // Cooperative loads of one key tile: unit u = r * threads + tid of each
+  // tensor is 16 bytes of block u / UPB of the tile.  Two register sets hold
+  // the next two tiles; a tile index past the end re-reads the last tile so
+  // that the loads are unconditional and each wait covers only its own set.
+  u32x4 pk0[UPT], pv0[UPT], pk1[UPT], pv1[UPT];
+  bool bad_id = false;
+  auto fetch = [&](u32x4 (&pk)[UPT], u32x4 (&pv)[UPT], int t) {
+    t = min(t, n_tiles - 1);
+#pragma unroll
+    for (int r = 0; r < UPT; ++r) {
+      const int u = r * kPrefillThreads + tid;
+      // The block of a unit is the same for the whole wave (UPB is a multiple
+      // of 64), so the table entry is a scalar load, which does not share the
+      // vector-load counter the K/V waits use.
+      const int lb = t * kTileBlocks + (r * kPrefillThreads + w * 64) / UPB;
+      const int wu = u % UPB;
+      // Blocks past the sequence end read its last block (always valid); the
+      // stash zeroes them.
+      int id = __builtin_amdgcn_readfirstlane(bt[min(lb, nb_seq - 1)]);
+      if (id < 0 || id >= a.num_blocks) {
+        bad_id |= lb < nb_seq;
+        id = 0;
+      }
+      const int64_t base = static_cast<int64_t>(id) * blk_elems + head_off;
+      pk[r] = *reinterpret_cast<const u32x4*>(a.k_cache + base + (wu / (D / 8)) * D + (wu % (D / 8)) * 8);
+      pv[r] = *reinterpret_cast<const u32x4*>(a.v_cache + base + static_cast<int64_t>(wu) * 8);
+    }
+  };
+  // Registers -> LDS.  V slots past the sequence end are zeroed (they may
+  // hold stale data, and 0 * NaN would leak into P.V).
+  auto stash = [&](const u32x4 (&pk)[UPT], const u32x4 (&pv)[UPT], int t) {
+#pragma unroll
+    for (int r = 0; r < UPT; ++r) {
+      const int u = r * kPrefillThreads + tid;
+      const int b = u / UPB;
+      const int wu = u % UPB;
+      const int kt = b * kBlock + wu / (D / 8);               // key within the tile
+      const int row = (kt & 32) | swap_bits23(kt & 31);
+      const bool live = t * kTileBlocks + b < nb_seq;
+      *reinterpret_cast<u32x4*>(lds + row * Lds::kRow + (wu % (D / 8)) * 16) = live ? pk[r] : u32x4{0, 0, 0, 0};
+      const int dim = wu >> 1;
+      const int h16 = wu & 1;
+      u32x4 v = pv[r];
+      const int n_ok = L - ((t * kTileBlocks + b) * kBlock + 8 * h16);   // keys of these 8 in range
+      if (n_ok <= 0) {
+        v = u32x4{0, 0, 0, 0};
+      } else if (n_ok < 8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t x = v[e];
+          if (2 * e >= n_ok) x &= 0xffff0000u;
+          if (2 * e + 1 >= n_ok) x &= 0x0000ffffu;
+          v[e] = x;
+        }
+      }
+      *reinterpret_cast<u32x4*>(lds + Lds::kBytesK + b * Lds::kBytesVBlock + dim * Lds::kVRow + h16 * 16) = v;
+    }
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[DT];
@@ -106,125 +203,131 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  bool poison = false;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int k0 = kt * 32;
-    const int lb0 = k0 / kBlock;
-    int p0 = bt[lb0];
-    int p1 = (lb0 + 1 < nb_seq) ? bt[lb0 + 1] : -1;
-    if (p0 < 0 || p0 >= a.num_blocks) { poison = true; p0 = 0; }
-    if (lb0 + 1 < nb_seq && (p1 < 0 || p1 >= a.num_blocks)) { poison = true; p1 = 0; }
+  // One key tile: S^T, online softmax, P.V, all from LDS.
+  auto compute = [&](int t) {
+    const int k0 = t * kTileKeys;
+    if (!wave_on || k0 > wave_lim) return;
 
-    // K operand: key r32 of the tile (block r32/16, slot r32%16), dims
-    // 16*ks + 8*half .. +7.
-    const int pk = (r32 < kBlock) ? p0 : p1;
-    u32x4 kr[KS];
-    if (pk >= 0) {
-      const uint16_t* kp = a.k_cache + pk * blk_elems + head_off + (r32 & 15) * D + 8 * half;
+    // S^T for the two 32-key halves of the tile.
+    f32x16 s[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const u32x4*>(kp + 16 * ks);
+    for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[c2][i] = 0.f;
+      const unsigned char* kr = lds + (32 * c2 + r32) * Lds::kRow + 16 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[c2] = mfma32x32x16<T>(*reinterpret_cast<const u32x4*>(kr + 32 * ks), qb[ks], s[c2]);
+    }
+
+    // Element i of half c2 in this lane is key k0 + 32*c2 + 16*(i/8) + 8*half + i%8.
+    // Only tiles that cross some row's last visible key need the mask.
+    const bool need_mask = k0 + kTileKeys - 1 > wave_lim_lo;
+    float mx = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * c2 + 16 * (i / 8) + 8 * half + (i % 8);
+          s[c2][i] = (key <= lim) ? s[c2][i] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[c2][i]);
+        }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[ks] = u32x4{0, 0, 0, 0};
-    }
-    f32x16 sacc;
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sacc = mfma32x32x16<T>(kr[ks], qb[ks], sacc);
-
-    // Element i of this lane is key k0 + 8*(i/4) + 4*half + i%4 of row my_row.
-    float sc[16];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + 8 * (i / 4) + 4 * half + (i % 4);
-      sc[i] = (key <= lim) ? sacc[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sc[i]);
+        for (int i = 0; i < 16; ++i) {
+          s[c2][i] *= a.scale_log2;
+          mx = fmaxf(mx, s[c2][i]);
+        }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = fast_exp2(m_run - m_new);
-    uint16_t pbits[16], plo[16];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pe = fast_exp2(sc[i] - m_new);
-      pbits[i] = from_f32<T>(pe);
-      float pr = to_f32<T>(pbits[i]);
-      if constexpr (SplitP<T>::kSplit) {
-        plo[i] = from_f32<T>(pe - pr);
-        pr += to_f32<T>(plo[i]);
-      }
-      psum += pr;
-    }
-    l_run = l_run * alpha + psum;
     m_run = m_new;
+    // The row sum adds the unrounded weights.  bf16 weights enter P.V as
+    // hi + lo halves that reproduce each weight to about 2^-17, and fp16
+    // weights to 2^-12, so the normalisation stays consistent with P.V to far
+    // below the output's own rounding.
+    float psum = 0.f;
+    u32x4 pB[4], pBl[4];             // P^T operands of the four 16-key k-steps
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-
-    // P^T operand for k-step ks: this lane's elements 8*ks .. 8*ks+7.
-    u32x4 pB[2], pBl[2];
+      for (int cc = 0; cc < 2; ++cc) {
+        uint16_t hi[8], lo[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      pB[ks] = u32x4{pack2(pbits[8 * ks + 0], pbits[8 * ks + 1]), pack2(pbits[8 * ks + 2], pbits[8 * ks + 3]),
-                     pack2(pbits[8 * ks + 4], pbits[8 * ks + 5]), pack2(pbits[8 * ks + 6], pbits[8 * ks + 7])};
-      pBl[ks] = u32x4{pack2(plo[8 * ks + 0], plo[8 * ks + 1]), pack2(plo[8 * ks + 2], plo[8 * ks + 3]),
-                      pack2(plo[8 * ks + 4], plo[8 * ks + 5]), pack2(plo[8 * ks + 6], plo[8 * ks + 7])};
-    }
-
-    // V^T operand for k-step ks (= block ks of the tile): dim 32*t + r32,
-    // slots 4*half .. +3 and 8 + 4*half .. +3 (the same key order as P^T).
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int pv = ks ? p1 : p0;
-      if (pv < 0) continue;                              // whole block past the end
-      const int kbase = k0 + 16 * ks;
-      const int valid = L - kbase;                       // keys of this block in range
-      const uint16_t* vp = a.v_cache + pv * blk_elems + head_off + r32 * kBlock + 4 * half;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const uint16_t* vt = vp + static_cast<int64_t>(32 * t) * kBlock;
-        u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
-        u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 8);
-        if (valid < kBlock) {
-          // Slots past the sequence end hold stale data (possibly NaN).
-          const int s0 = 4 * half;
-          uint32_t w0 = lo[0], w1 = lo[1], w2 = hi[0], w3 = hi[1];
-          if (s0 + 0 >= valid) w0 &= 0xffff0000u;
-          if (s0 + 1 >= valid) w0 &= 0x0000ffffu;
-          if (s0 + 2 >= valid) w1 &= 0xffff0000u;
-          if (s0 + 3 >= valid) w1 &= 0x0000ffffu;
-          if (s0 + 8 >= valid) w2 &= 0xffff0000u;
-          if (s0 + 9 >= valid) w2 &= 0x0000ffffu;
-          if (s0 + 10 >= valid) w3 &= 0xffff0000u;
-          if (s0 + 11 >= valid) w3 &= 0x0000ffffu;
-          lo = u32x2{w0, w1};
-          hi = u32x2{w2, w3};
+        for (int j = 0; j < 8; ++j) {
+          const float pe = fast_exp2(s[c2][8 * cc + j] - m_new);
+          hi[j] = from_f32<T>(pe);
+          if constexpr (SplitP<T>::kSplit) {
+            lo[j] = from_f32<T>(pe - to_f32<T>(hi[j]));
+          } else {
+            lo[j] = 0;
+          }
+          psum += pe;
         }
-        const u32x4 vA = {lo[0], lo[1], hi[0], hi[1]};
-        o[t] = mfma32x32x16<T>(vA, pB[ks], o[t]);
-        if constexpr (SplitP<T>::kSplit) o[t] = mfma32x32x16<T>(vA, pBl[ks], o[t]);
+        pB[2 * c2 + cc] = u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
+        pBl[2 * c2 + cc] = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+
+    // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys 8*half .. +7.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const unsigned char* vr = lds + Lds::kBytesK + kk * Lds::kBytesVBlock + r32 * Lds::kVRow + 16 * half;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 vA = *reinterpret_cast<const u32x4*>(vr + 32 * dt * Lds::kVRow);
+        o[dt] = mfma32x32x16<T>(vA, pB[kk], o[dt]);
+        if constexpr (SplitP<T>::kSplit) o[dt] = mfma32x32x16<T>(vA, pBl[kk], o[dt]);
       }
     }
-  }
+  };
 
+  // Tiles go in pairs, one per register set, with a single exit test at the
+  // bottom (an odd count gets one more, fully masked tile whose compute
+  // returns at once): a break between the two halves would merge a path on
+  // which set 1 was never loaded into the loop header and force every wait
+  // there to drain all loads.
+  fetch(pk0, pv0, 0);
+  __builtin_amdgcn_sched_barrier(0);   // keep set 0's loads older than set 1's
+  fetch(pk1, pv1, 1);
+  int t = 0;
+  do {
+    __syncthreads();                 // every wave is done with the previous tile
+    stash(pk0, pv0, t);
+    __syncthreads();                 // tile t is in LDS
+    fetch(pk0, pv0, t + 2);
+    compute(t);
+    __syncthreads();
+    stash(pk1, pv1, t + 1);
+    __syncthreads();
+    fetch(pk1, pv1, t + 3);
+    compute(t + 1);
+    t += 2;
+  } while (t < n_tiles);
+
+  const bool poison = __syncthreads_or(bad_id);
   l_run += __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const float inv_nan = poison ? NAN : 0.f;
   uint16_t* op = a.out + out_row * D;
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      // elements 4*q4 .. 4*q4+3: dims 32*t + 8*q4 + 4*half + 0..3
+      // elements 4*q4 .. 4*q4+3: dims 32*dt + 8*q4 + 4*half + 0..3
       uint16_t r[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = from_f32<T>(o[t][4 * q4 + e] / l_run + inv_nan);
-      *reinterpret_cast<u32x2*>(op + 32 * t + 8 * q4 + 4 * half) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
+      for (int e = 0; e < 4; ++e) r[e] = from_f32<T>(o[dt][4 * q4 + e] / l_run + inv_nan);
+      *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q4 + 4 * half) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
     }
 }
 
@@ -232,10 +335,10 @@ template <class T, int D>
 hipError_t launch_td(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.group;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int wg_rows = 32 * (4 / hpw);
+  const int wg_rows = 32 * (kPrefillWaves / hpw);
   const int n_rb = (a.max_q_len + wg_rows - 1) / wg_rows;
   const dim3 grid(n_rb, a.num_chunks, a.num_kv_heads * (G / hpw));
-  hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kPrefillThreads), 0, stream, a);
   return hipGetLastError();
 }
 
