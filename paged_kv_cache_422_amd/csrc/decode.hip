@@ -347,7 +347,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Second pass: one wave per (sequence, query head) with more than one
 // partition.  m = max_p m_p; l = sum_p l_p 2^(m_p - m);
-// o = sum_p acc_p 2^(m_p - m) / l, partitions in index order.
+// o = sum_p acc_p 2^(m_p - m) / l, partitions in index order.  Lane p holds
+// partition p's (m_p, l_p) (lanes take partitions p, p + 64, ... when there
+// are more than 64), so the state is read once, and the accumulator loads of
+// four partitions are in flight together.
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -358,20 +361,33 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (np <= 1) return;
   const float* ml = a.ws_ml + row * a.max_parts * 2;
   const float* acc = a.ws_acc + row * a.max_parts * D;
-  float M = -INFINITY;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
+  const float m0 = lane < np ? ml[2 * lane] : -INFINITY;
+  const float l0 = lane < np ? ml[2 * lane + 1] : 0.f;
+  float M = m0;
+  for (int p = lane + 64; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
   M = wave_max(M);
-  float lsum = 0.f;
-  for (int p = lane; p < np; p += 64) lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  const float w0 = fast_exp2(m0 - M);          // weight of partition `lane`
+  float lsum = l0 * w0;
+  for (int p = lane + 64; p < np; p += 64) lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
   lsum = wave_sum(lsum);
   constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float f = fast_exp2(ml[2 * p] - M);
+  for (int p0 = 0; p0 < np; p0 += 4) {
+    float v[4][PER], f[4];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] += acc[static_cast<int64_t>(p) * D + lane + 64 * i] * f;
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + k;
+      f[k] = p >= np ? 0.f : p < 64 ? __shfl(w0, p) : fast_exp2(ml[2 * p] - M);
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        v[k][i] = p < np ? acc[static_cast<int64_t>(p) * D + lane + 64 * i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += v[k][i] * f[k];
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) a.out[row * D + lane + 64 * i] = from_f32<T>(o[i] / lsum);
