@@ -1,0 +1,44 @@
+"""bench.py logic that needs no GPU: the single-GPU contract and the rule
+that HBM traffic is reported only for the kernel source it was measured on."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_metric_is_the_baseline_metric():
+    import json
+    with open(os.path.join(ROOT, "BASELINE.json")) as f:
+        assert bench.METRIC == json.load(f)["metric"]
+
+
+def test_traffic_requires_matching_source_hash(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    digest = hashlib.sha256(b"kernel v1\n").hexdigest()
+    (prof / "x_pmc.md").write_text(f"notes\ntraffic_bytes_per_launch: 12345\nsource_sha256: {digest}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.profiled_traffic("x_pmc.md", ("k.hip",)) == 12345
+    src.write_text("kernel v2\n")                      # the kernel changed since profiling
+    assert bench.profiled_traffic("x_pmc.md", ("k.hip",)) is None
+    assert bench.profiled_traffic("missing.md", ("k.hip",)) is None
+
+
+def test_committed_decode_profiles_parse():
+    for wl in ("llama7b", "llama8b_gqa"):
+        path = os.path.join(ROOT, "profiles", f"decode_{wl}_pmc.md")
+        text = open(path).read()
+        assert "traffic_bytes_per_launch:" in text and "source_sha256:" in text
