@@ -322,6 +322,19 @@ def main():
     dec_ms = mean(per[-1])                       # pa_decode is the last call of every step
     gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
 
+    if name == "llama8b_gqa" and P != 0:
+        # The workload fixes 512-token split-KV partitions; also time the same
+        # batch with the library's default partitioning for comparison.
+        P_def = pa.default_partition_size(num_seqs, Hq, Hkv, D, w.max_model_len)
+        ws_def = torch.empty(max(pa.decode_workspace_size(w.num_seqs, Hq, D, w.max_model_len, 0, Hkv), 1),
+                             dtype=torch.uint8, device="cuda")
+        fn_def = [lambda: pa.decode(out, q, kc, vc, bt, ctx, w.max_model_len, w.scale, 0, ws_def)]
+        timer.run(args.warmup, fn_def)
+        _, tot_def, _ = timer.run(args.steps, fn_def)
+        gbs_def = kv_bytes / (mean(tot_def) * 1e-3) / 1e9
+        extra["library_default_partition"] = {"partition_size": P_def, "us_per_step": round(mean(tot_def) * 1e3, 2),
+                                              "GB/s": round(gbs_def, 2), "frac_hbm": round(gbs_def / HBM_PEAK_GBS, 4)}
+
     if name == "mixed":
         w_ms, p_ms = mean(per[0]), mean(per[1])
         extra["calls_us"] = {"write_kv": round(w_ms * 1e3, 2), "prefill_chunk": round(p_ms * 1e3, 2),
@@ -368,7 +381,7 @@ def main():
                            if name == "mixed" else ""),
             "num_seqs": num_seqs,
             "kv_bytes_per_step": int(kv_bytes),
-            "partition_size": P or pa.default_partition_size(Hq, Hkv, D),
+            "partition_size": P or pa.default_partition_size(num_seqs, Hq, Hkv, D, w.max_model_len),
             "cache": "warm" if args.warm_cache else "Infinity Cache evicted before each step",
             "parallelism": "none (1 GPU)",
         },

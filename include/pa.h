@@ -112,18 +112,22 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
  *                   above max_context_len or bt_stride*block_size gives NaN.
  *   max_context_len host-side upper bound of context_lens (sizes the grid).
  *   scale           softmax scale (usually 1/sqrt(head_dim)).
- *   partition_size  long contexts are cut into partitions of this many
- *                   tokens, each handled by its own workgroup, and merged by
- *                   log-sum-exp in a second kernel.  0 = library default
- *                   (pa_default_partition_size).  Multiple of 16, <= 4096.
+ *   partition_size  long contexts are cut into partitions of at most this
+ *                   many tokens (ceil(L / partition_size) partitions of
+ *                   nearly equal size), each handled by its own workgroup,
+ *                   and merged by log-sum-exp in a second kernel.  0 =
+ *                   library default (pa_default_partition_size: no split when
+ *                   num_seqs * num_kv_heads already gives >= 1024 work items,
+ *                   else just enough split to reach that many).  Multiple of
+ *                   16, <= 4096.
  *                   The result for a sequence depends only on its own data
  *                   and on the partition size, never on the rest of the batch.
  *   workspace       device scratch of at least pa_decode_workspace_size()
  *                   bytes for the same arguments (may be NULL if that size is
  *                   0); contents need not be initialised.
  * ---------------------------------------------------------------------- */
-int32_t   pa_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads,
-                                    int32_t head_dim);
+int32_t   pa_default_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_context_len);
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t partition_size,
                                    int32_t num_kv_heads, size_t* bytes);

@@ -44,7 +44,7 @@ _SIGS = {
     "pa_write_kv": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32,
                             c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
-    "pa_default_partition_size": (c_i32, [c_i32, c_i32, c_i32]),
+    "pa_default_partition_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_workspace_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          ctypes.POINTER(c_sz)]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
@@ -130,8 +130,10 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None):
                                H, D, B, _dtype_code(k_cache), _stream(stream)))
 
 
-def default_partition_size(num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
-    return int(_lib.pa_default_partition_size(num_q_heads, num_kv_heads, head_dim))
+def default_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_context_len: int) -> int:
+    return int(_lib.pa_default_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len))
 
 
 def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,

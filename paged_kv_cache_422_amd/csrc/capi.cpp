@@ -61,20 +61,25 @@ pa_status hip_result(const char* fn, hipError_t e) {
   return ok();
 }
 
-// Blocks each decode wave keeps in flight.  PA_DECODE_DEPTH (1 or 2)
-// overrides the default for experiments; it is read once per process.
-int32_t decode_depth() {
-  static const int32_t depth = [] {
-    const char* e = std::getenv("PA_DECODE_DEPTH");
-    if (e && (e[0] == '1' || e[0] == '2') && e[1] == '\0') return static_cast<int32_t>(e[0] - '0');
-    return static_cast<int32_t>(2);
+// Waves that share one decode partition: 8 for partitions of 128 blocks or
+// more (a long partition then finishes about as fast as a 64-block one with
+// 4 waves, which keeps the end of the launch short), else 4.  PA_DECODE_WAVES
+// (4 or 8) overrides the choice for experiments; it is read once per process.
+int32_t decode_waves(int32_t part_blocks) {
+  static const int32_t forced = [] {
+    const char* e = std::getenv("PA_DECODE_WAVES");
+    if (e && (e[0] == '4' || e[0] == '8') && e[1] == '\0') return static_cast<int32_t>(e[0] - '0');
+    return static_cast<int32_t>(0);
   }();
-  return depth;
+  if (forced) return forced;
+  return part_blocks >= 128 ? 8 : 4;
 }
 
-int32_t resolve_partition(int32_t requested, int32_t num_q_heads, int32_t num_kv_heads,
-                          int32_t head_dim) {
-  return requested > 0 ? requested : pa_default_partition_size(num_q_heads, num_kv_heads, head_dim);
+int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
+  return requested > 0 ? requested
+                       : pa_default_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                   max_context_len);
 }
 
 }  // namespace
@@ -124,16 +129,24 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, const
 }
 
 // Every partition beyond a sequence's first writes a partial state (head_dim
-// + 2 floats per query head) that the second pass reads back.  On MI355X those
-// writes cost about ten times their size in lost read bandwidth, so the
-// default keeps partitions long: 1024 tokens (64 blocks, 16 per wave) still
-// leaves several workgroups per (sequence, KV head) for contexts of a few
-// thousand tokens while halving the partial traffic of 512.
-int32_t pa_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
-  (void)num_q_heads;
-  (void)num_kv_heads;
+// + 2 floats per query head) that the second pass reads back, and on MI355X
+// those writes cost about ten times their size in lost read bandwidth.  So a
+// batch that already offers enough (sequence, KV head) work items to fill
+// the GPU many times over (kTargetItems) is not split at all; a smaller batch
+// is split just enough to reach that many items.  Partitions are whole
+// multiples of 16 tokens between 256 and 4096.
+constexpr int64_t kTargetItems = 1024;
+
+int32_t pa_default_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_context_len) {
   (void)head_dim;
-  return 1024;
+  const int64_t group = num_kv_heads > 0 && num_q_heads > 0 ? num_q_heads / num_kv_heads : 1;
+  const int64_t rows = std::max<int64_t>(1, static_cast<int64_t>(num_seqs) * num_kv_heads *
+                                                ((group + 15) / 16));
+  const int64_t parts = std::max<int64_t>(1, (kTargetItems + rows - 1) / rows);
+  int64_t P = (std::max<int64_t>(max_context_len, 1) + parts - 1) / parts;
+  P = (P + kBlock - 1) / kBlock * kBlock;
+  return static_cast<int32_t>(std::min<int64_t>(kMaxPartitionTokens, std::max<int64_t>(256, P)));
 }
 
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -143,7 +156,8 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
       partition_size < 0 || num_kv_heads <= 0)
     return fail(PA_EINVAL, "pa_decode_workspace_size: bad size");
-  const int32_t P = resolve_partition(partition_size, num_q_heads, num_kv_heads, head_dim);
+  const int32_t P = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      max_context_len);
   const int64_t max_parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
   if (max_parts <= 1) {
     *bytes = 0;
@@ -175,7 +189,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ENOTSUP, "pa_decode: 16-byte alignment required");
   if (num_seqs > 65535) return fail(PA_ENOTSUP, "pa_decode: at most 65535 sequences per call");
-  const int32_t P = resolve_partition(partition_size, num_q_heads, num_kv_heads, head_dim);
+  const int32_t P = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      max_context_len);
   size_t need = 0;
   if (pa_status st = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                               P, num_kv_heads, &need))
@@ -211,7 +226,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.part_blocks = P / kBlock;
   a.max_parts = static_cast<int32_t>(max_parts);
   a.max_context_len = max_context_len;
-  a.depth = decode_depth();
+  a.waves = decode_waves(a.part_blocks);
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_result(fn, pa::launch_decode(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
 }

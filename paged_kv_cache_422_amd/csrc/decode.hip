@@ -50,7 +50,6 @@ namespace pa {
 namespace {
 
 constexpr int kBlock = 16;   // tokens per KV block == MFMA tile edge
-constexpr int kWaves = 4;
 constexpr int kBtRegs = 4;   // block-table registers per lane: partitions up to 256 blocks
 
 // -1: invalid context length; 0: empty; otherwise number of partitions.
@@ -82,22 +81,17 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* k
     r.v[t] = *reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t);
 }
 
-// Occupancy target per pipeline depth: DEPTH blocks in flight per wave need
-// (DEPTH + 1) register buffers; depth 1 fits three waves per SIMD, depth 2
-// two.
-template <int DEPTH> struct DecodeOcc;
-template <> struct DecodeOcc<1> { static constexpr int kWavesPerEU = 3; };
-template <> struct DecodeOcc<2> { static constexpr int kWavesPerEU = 2; };
-
-template <class T, int D, int NH, int DEPTH>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(DecodeOcc<DEPTH>::kWavesPerEU, DecodeOcc<DEPTH>::kWavesPerEU)))
+// W waves share one partition (W = 4 or 8); each keeps two blocks in flight
+// in three register buffers, which fits two waves per SIMD.
+template <class T, int D, int NH, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;
   constexpr int VT = D / 16;
-  __shared__ float sm_m[kWaves][NH];
-  __shared__ float sm_l[kWaves][NH];
-  __shared__ float sm_o[kWaves][NH][D];
+  constexpr int kThreads = 64 * W;
+  __shared__ float sm_m[W][NH];
+  __shared__ float sm_l[W][NH];
+  __shared__ float sm_o[W][NH][D];
 
   // blockIdx.x = (part * num_seqs + s) * (num_kv_heads * num_sub) + head group
   const int n_hg = a.num_kv_heads * a.num_sub;
@@ -121,7 +115,7 @@ void decode_partition_kernel(DecodeArgs a) {
     // Empty context: zero rows.  Invalid length: NaN rows.  Partition 0 only.
     if (part == 0) {
       const uint16_t fill = np == 0 ? uint16_t(0) : from_f32<T>(NAN);
-      for (int i = tid; i < nh * D; i += 256)
+      for (int i = tid; i < nh * D; i += kThreads)
         a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + i / D) * D + i % D] = fill;
     }
     return;
@@ -239,9 +233,8 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // Software pipeline over DEPTH + 1 register buffers: the loads of the
-  // next DEPTH blocks a wave handles are in flight while it works on the
-  // current one.  Prefetches are issued unconditionally (past the end they
+  // Software pipeline over three register buffers: the loads of the next two
+  // blocks a wave handles are in flight while it works on the current one.  Prefetches are issued unconditionally (past the end they
   // re-read the wave's last block, which the cache still holds) so that the
   // wait before each block only covers that block's own loads.
   auto blk_off = [&](int jj) {
@@ -253,40 +246,25 @@ void decode_partition_kernel(DecodeArgs a) {
     return static_cast<int64_t>(id) * blk_elems;
   };
   int j = w;
-  const int j_last = w + ((nblk - 1 - w) / kWaves) * kWaves;   // this wave's last block
+  const int j_last = w + ((nblk - 1 - w) / W) * W;   // this wave's last block
   auto nxt = [&](int jj) { return jj < nblk ? jj : j_last; };
   if (j < nblk) {
-    if constexpr (DEPTH == 1) {
-      BlockRegs<T, D> b0, b1;
-      load_block<T, D>(b0, kbase, vbase, blk_off(j));
-      for (;;) {
-        load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + kWaves)));
-        process(b0, j);
-        j += kWaves;
-        if (j >= nblk) break;
-        load_block<T, D>(b0, kbase, vbase, blk_off(nxt(j + kWaves)));
-        process(b1, j);
-        j += kWaves;
-        if (j >= nblk) break;
-      }
-    } else {
-      BlockRegs<T, D> b0, b1, b2;
-      load_block<T, D>(b0, kbase, vbase, blk_off(j));
-      load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + kWaves)));
-      for (;;) {
-        load_block<T, D>(b2, kbase, vbase, blk_off(nxt(j + 2 * kWaves)));
-        process(b0, j);
-        j += kWaves;
-        if (j >= nblk) break;
-        load_block<T, D>(b0, kbase, vbase, blk_off(nxt(j + 2 * kWaves)));
-        process(b1, j);
-        j += kWaves;
-        if (j >= nblk) break;
-        load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + 2 * kWaves)));
-        process(b2, j);
-        j += kWaves;
-        if (j >= nblk) break;
-      }
+    BlockRegs<T, D> b0, b1, b2;
+    load_block<T, D>(b0, kbase, vbase, blk_off(j));
+    load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + W)));
+    for (;;) {
+      load_block<T, D>(b2, kbase, vbase, blk_off(nxt(j + 2 * W)));
+      process(b0, j);
+      j += W;
+      if (j >= nblk) break;
+      load_block<T, D>(b0, kbase, vbase, blk_off(nxt(j + 2 * W)));
+      process(b1, j);
+      j += W;
+      if (j >= nblk) break;
+      load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + 2 * W)));
+      process(b2, j);
+      j += W;
+      if (j >= nblk) break;
     }
   }
 
@@ -306,15 +284,15 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   __syncthreads();
 
-  for (int i = tid; i < nh * D; i += 256) {
+  for (int i = tid; i < nh * D; i += kThreads) {
     const int h = i / D;
     const int d = i - h * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][h]);
+    for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v][h]);
     float lsum = 0.f, acc = 0.f;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = 0; v < W; ++v) {
       const float f = fast_exp2(sm_m[v][h] - M);
       lsum += sm_l[v][h] * f;
       acc += sm_o[v][h][d] * f;
@@ -397,10 +375,10 @@ template <class T, int D, int NH>
 hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
   const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
   const dim3 grid(static_cast<uint32_t>(n_wg));
-  if (a.depth == 1)
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 1>), grid, dim3(256), 0, stream, a);
+  if (a.waves == 8)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 8>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 2>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 4>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;

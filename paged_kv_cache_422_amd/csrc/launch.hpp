@@ -48,7 +48,7 @@ struct DecodeArgs {
   int32_t part_blocks;        // partition size in blocks
   int32_t max_parts;
   int32_t max_context_len;
-  int32_t depth;              // blocks in flight per wave (1 or 2)
+  int32_t waves;              // waves sharing one partition (4 or 8)
   float scale_log2;           // scale * log2(e)
 };
 

@@ -87,7 +87,18 @@ def test_workspace_size_formula():
     assert pa.decode_workspace_size(64, 32, 128, 2048, 512, 32) == 64 * 32 * 4 * 130 * 4
     assert pa.decode_workspace_size(64, 32, 128, 512, 512, 32) == 0
     assert pa.decode_workspace_size(3, 4, 64, 100, 16, 4) == 3 * 4 * 7 * 66 * 4
-    assert pa.default_partition_size(32, 8, 128) % 16 == 0
+    assert pa.default_partition_size(64, 32, 8, 128, 4096) % 16 == 0
+
+
+def test_default_partition_follows_available_parallelism():
+    # enough (sequence, KV head) rows: one partition per sequence (capped at 4096)
+    assert pa.default_partition_size(64, 32, 32, 128, 2048) == 2048
+    assert pa.default_partition_size(256, 32, 8, 128, 4096) == 4096
+    assert pa.default_partition_size(4096, 32, 8, 128, 8192) == 4096
+    # few rows: split until about 1024 items, never below 256 tokens
+    assert pa.default_partition_size(1, 32, 8, 128, 32768) == 256
+    assert pa.default_partition_size(8, 32, 8, 128, 32768) == 2048
+    assert pa.default_partition_size(4, 4, 4, 64, 128) == 256
 
 
 # ---------------------------------------------------------------------------
