@@ -19,36 +19,84 @@ namespace {
 
 constexpr int kBlock = 16;   // tokens per KV block
 
-// One thread per (token, kv head, 8-element chunk of the head dim): one
-// 16-byte load of k and v, one 16-byte store into the K tile row, eight
-// 2-byte stores down the V tile's slot column.
-__global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
-  const int chunks = a.head_dim >> 3;
-  const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * chunks;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= per_token * a.num_tokens) return;
-  const int64_t tok = idx / per_token;
-  const int rem = static_cast<int>(idx - tok * per_token);
-  const int head = rem / chunks;
-  const int chunk = rem - head * chunks;
+// One workgroup per (16 consecutive tokens, kv head), 2 * D threads.
+//
+// K: thread (chunk c, token i) moves one 16-byte piece of token i's K row.
+// V: a V row of a block is the 16 slots of one dim (32 bytes), so a single
+// token only touches 2 bytes of it.  The group's values pass through LDS,
+// transposed to [dim][token]; thread (dim d, half h) then owns tokens
+// 8h .. 8h+7 of dim d.  When those eight tokens go to eight consecutive slots
+// starting at a multiple of 8 (prefill chunks fill their blocks in order) the
+// thread stores them as one 16-byte piece, and its neighbour (the other half)
+// completes the 32-byte row in the same instruction, so HBM sees whole
+// sectors.  Any other mapping (decode tokens, each alone in its block, or
+// skipped tokens) falls back to one 2-byte store per token.
+template <int D>
+__global__ __launch_bounds__(2 * D) void write_kv_kernel(WriteKvArgs a) {
+  constexpr int kChunks = D / 8;
+  __shared__ int64_t slot_s[kBlock];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D * kBlock];   // [dim][token]
 
-  const int64_t slot = a.slot_mapping[tok];
-  if (slot < 0 || slot >= a.num_blocks * kBlock) return;   // skipped token
-  const int64_t blk = slot / kBlock;
-  const int off = static_cast<int>(slot - blk * kBlock);
+  const int tid = threadIdx.x;
+  const int head = blockIdx.y;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBlock;
+  const int nt = static_cast<int>(min<int64_t>(kBlock, a.num_tokens - t0));
+  const int64_t limit = a.num_blocks * kBlock;
+  if (tid < kBlock) {
+    int64_t sl = -1;
+    if (tid < nt) {
+      sl = a.slot_mapping[t0 + tid];
+      if (sl < 0 || sl >= limit) sl = -1;                       // skipped token
+    }
+    slot_s[tid] = sl;
+  }
 
-  const int64_t src = tok * a.src_token_stride + static_cast<int64_t>(head) * a.head_dim + chunk * 8;
-  const u32x4 kk = *reinterpret_cast<const u32x4*>(a.k + src);
-  const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v + src);
-
-  const int64_t tile = (blk * a.num_kv_heads + head) * static_cast<int64_t>(kBlock) * a.head_dim;
-  *reinterpret_cast<u32x4*>(a.k_cache + tile + static_cast<int64_t>(off) * a.head_dim + chunk * 8) = kk;
-
-  uint16_t* vcol = a.v_cache + tile + static_cast<int64_t>(chunk * 8) * kBlock + off;
+  const int i = tid % kBlock;          // token within the group
+  const int c = tid / kBlock;          // 8-element chunk of the head dim
+  u32x4 kk{0, 0, 0, 0}, vv{0, 0, 0, 0};
+  if (i < nt) {
+    const int64_t src = (t0 + i) * a.src_token_stride + static_cast<int64_t>(head) * D + c * 8;
+    kk = *reinterpret_cast<const u32x4*>(a.k + src);
+    vv = *reinterpret_cast<const u32x4*>(a.v + src);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    vcol[(2 * e) * kBlock] = static_cast<uint16_t>(vv[e] & 0xffffu);
-    vcol[(2 * e + 1) * kBlock] = static_cast<uint16_t>(vv[e] >> 16);
+    vt[(c * 8 + 2 * e) * kBlock + i] = static_cast<uint16_t>(vv[e] & 0xffffu);
+    vt[(c * 8 + 2 * e + 1) * kBlock + i] = static_cast<uint16_t>(vv[e] >> 16);
+  }
+  __syncthreads();
+
+  const int64_t head_tile = static_cast<int64_t>(head) * kBlock * D;
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * kBlock * D;
+  {
+    const int64_t sl = slot_s[i];
+    if (sl >= 0) {
+      const int64_t blk = sl / kBlock;
+      const int off = static_cast<int>(sl - blk * kBlock);
+      *reinterpret_cast<u32x4*>(a.k_cache + blk * blk_elems + head_tile + off * D + c * 8) = kk;
+    }
+  }
+
+  const int d = tid >> 1;
+  const int h = tid & 1;
+  const int64_t s0 = slot_s[8 * h];
+  bool run = s0 >= 0 && (s0 & 7) == 0;
+#pragma unroll
+  for (int j = 1; j < 8; ++j) run = run && slot_s[8 * h + j] == s0 + j;
+  if (run) {
+    const int64_t blk = s0 / kBlock;
+    const int off = static_cast<int>(s0 - blk * kBlock);        // 0 or 8
+    *reinterpret_cast<u32x4*>(a.v_cache + blk * blk_elems + head_tile + d * kBlock + off) =
+        *reinterpret_cast<const u32x4*>(&vt[d * kBlock + 8 * h]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t sl = slot_s[8 * h + j];
+      if (sl < 0) continue;
+      const int64_t blk = sl / kBlock;
+      const int off = static_cast<int>(sl - blk * kBlock);
+      a.v_cache[blk * blk_elems + head_tile + d * kBlock + off] = vt[d * kBlock + 8 * h + j];
+    }
   }
 }
 
@@ -73,9 +121,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
 }  // namespace
 
 hipError_t launch_write_kv(const WriteKvArgs& a, int /*dtype*/, hipStream_t stream) {
-  const int64_t threads = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * (a.head_dim / 8);
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(write_kv_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a);
+  if (a.num_kv_heads > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<uint32_t>((static_cast<int64_t>(a.num_tokens) + kBlock - 1) / kBlock),
+                  static_cast<uint32_t>(a.num_kv_heads));
+  if (a.head_dim == 64) {
+    hipLaunchKernelGGL(write_kv_kernel<64>, grid, dim3(128), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(write_kv_kernel<128>, grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -65,6 +65,18 @@ def test_prefill_shapes(dtype, Hq, Hkv, D):
     assert_close(out, want, what=f"prefill Hq={Hq} Hkv={Hkv} D={D}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_prefill_long_context(dtype):
+    """Cached context past 1024 blocks (16384 keys), so tiles take block ids
+    from beyond the kernel's on-chip copy of the table."""
+    chunks = [(20000 - 70, 70), (16384 - 16, 33), (300, 5)]
+    print(f"prefill long dtype={dtype}", flush=True)
+    q, kc, vc, bt, qsl, lens = prefill_case(chunks, 4, 2, 64, dtype, seed=77)
+    out = run_prefill(q, kc, vc, bt, qsl, lens, 0.125)
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, 0.125, dtype_name(q))
+    assert_close(out, want, what="prefill long context")
+
+
 def test_prefill_chunking_and_decode_agree():
     """Rows computed as one chunk, as two chunks, and the last row as a
     decode step all agree within tolerance of the oracle."""

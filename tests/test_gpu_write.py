@@ -42,6 +42,44 @@ def test_write_kv_bit_exact(dtype, H, D):
     assert np.array_equal(bits(vc).view(np.uint16), want_v.view(np.uint16))
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("H,D", [(8, 128), (3, 64)])
+def test_write_kv_runs_and_scattered_tokens(dtype, H, D):
+    """Token groups whose slots are whole aligned runs (prefill filling its
+    blocks in order), runs that start mid-block or cross blocks, runs with a
+    skipped token inside, lone decode tokens, and a ragged last group."""
+    print(f"write_kv runs dtype={dtype} H={H} D={D}", flush=True)
+    N = 64
+    rng = np.random.default_rng(9)
+    blocks = rng.permutation(N - 4)      # blocks N-4 .. N-1 are kept for the crossing run
+    lone = iter(int(b) * 16 + int(rng.integers(16)) for b in blocks[20:56])
+    run = lambda b, start, n: [int(b) * 16 + start + j for j in range(n)]
+    groups = [
+        run(blocks[0], 0, 16),                                  # whole block
+        run(blocks[1], 0, 16),
+        run(blocks[2], 8, 8) + [next(lone) for _ in range(8)],  # aligned half, then lone tokens
+        [next(lone) for _ in range(8)] + run(blocks[3], 0, 8),
+        run(blocks[4], 0, 16),                                  # run with a skipped token
+        run(blocks[5], 3, 13) + [next(lone) for _ in range(3)], # starts mid-block
+        run(N - 4, 5, 16),                                      # crosses into the next block
+        [next(lone) for _ in range(16)],                        # decode-like
+    ]
+    groups[4][4] = -1
+    slots = [x for grp in groups for x in grp] + run(blocks[6], 0, 11)   # ragged last group
+    slots = np.array(slots, dtype=np.int64)
+    T = len(slots)
+    g = torch.Generator(device=DEV).manual_seed(21)
+    k = torch.randn(T, H, D, generator=g, device=DEV).to(dtype)
+    v = torch.randn(T, H, D, generator=g, device=DEV).to(dtype)
+    kc, vc = _sentinel_cache(N, H, D, dtype)
+    want_k, want_v = bits(kc), bits(vc)
+    pa.write_kv(k, v, kc, vc, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    KC.write_kv(want_k, want_v, bits(k), bits(v), slots, 16)
+    assert np.array_equal(bits(kc).view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(bits(vc).view(np.uint16), want_v.view(np.uint16))
+
+
 def test_write_kv_strided_source():
     """k/v as views into a fused [T, 3, H, D] tensor (token stride 3*H*D)."""
     dtype, H, D, N, T = torch.bfloat16, 8, 128, 16, 50
