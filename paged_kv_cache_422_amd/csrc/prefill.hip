@@ -33,6 +33,7 @@
 // dim-major V block.  LDS rows are padded by 16 bytes so that the 16-byte
 // operand reads of a wave hit distinct banks.  Row tiles are dispatched
 // heaviest (longest causal range) first.
+#include <float.h>
 #include <math.h>
 
 #include "common.hpp"
@@ -61,6 +62,7 @@ __device__ __forceinline__ int swap_bits23(int r) {
 }
 
 constexpr int kPrefillWaves = 8;
+constexpr float kLazyLog2 = 8.f;      // running-maximum slack, log2 units
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
 template <class T, int D>
@@ -124,6 +126,19 @@ void prefill_kernel(PrefillArgs a) {
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+  }
+  // Logits enter the exponent as fma(s, c, -m) with c = |scale * log2(e)|,
+  // so the tile maximum can be taken on the raw products.  A negative scale
+  // is carried by Q instead: flipping its sign bits is exact, and the
+  // products come out exactly negated.  A zero scale becomes the smallest
+  // normal float, which leaves every weight at exactly 1 and keeps masked
+  // keys (-inf) at -inf rather than NaN.
+  const float c_log2 = a.scale_log2 == 0.f ? FLT_MIN : fabsf(a.scale_log2);
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qb[ks][e] ^= 0x80008000u;
   }
 
   const int wg_last_row = min(wg_row0 + wg_rows - 1, n - 1);
@@ -231,22 +246,34 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * c2 + 16 * (i / 8) + 8 * half + (i % 8);
-          s[c2][i] = (key <= lim) ? s[c2][i] * a.scale_log2 : -INFINITY;
+          s[c2][i] = (key <= lim) ? s[c2][i] : -INFINITY;
           mx = fmaxf(mx, s[c2][i]);
         }
     } else {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[c2][i] *= a.scale_log2;
-          mx = fmaxf(mx, s[c2][i]);
-        }
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[c2][i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    // Lazy rescaling: the running maximum moves only when the tile's exceeds
+    // it by more than kLazyLog2, so weights stay below 2^kLazyLog2 (the
+    // arithmetic is unchanged and fp32 has the range) and the accumulators
+    // are rescaled only when some row of the wave moves.  A row with no
+    // visible key in the tile has mx = -inf, which never moves.
+    const float mt = mx * c_log2;
+    const bool move = mt > m_run + kLazyLog2;
+    if (__ballot(move)) {
+      const float m_new = move ? mt : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    const float neg_m = -m_run;
     // The row sum adds the unrounded weights.  bf16 weights enter P.V as
     // hi + lo halves that reproduce each weight to about 2^-17, and fp16
     // weights to 2^-12, so the normalisation stays consistent with P.V to far
@@ -260,7 +287,7 @@ void prefill_kernel(PrefillArgs a) {
         uint16_t hi[8], lo[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float pe = fast_exp2(s[c2][8 * cc + j] - m_new);
+          const float pe = fast_exp2(fmaf(s[c2][8 * cc + j], c_log2, neg_m));   // masked: -inf
           hi[j] = from_f32<T>(pe);
           if constexpr (SplitP<T>::kSplit) {
             lo[j] = from_f32<T>(pe - to_f32<T>(hi[j]));
@@ -272,11 +299,7 @@ void prefill_kernel(PrefillArgs a) {
         pB[2 * c2 + cc] = u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
         pBl[2 * c2 + cc] = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    l_run += psum;
 
     // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys 8*half .. +7.
 #pragma unroll

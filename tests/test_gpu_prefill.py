@@ -77,6 +77,19 @@ def test_prefill_long_context(dtype):
     assert_close(out, want, what="prefill long context")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 3.0])
+def test_prefill_scale_sign_and_size(scale):
+    """A negative scale (carried by Q's sign), a zero scale (uniform weights
+    over the visible keys) and a large one (peaked weights, frequent moves of
+    the running maximum)."""
+    chunks = [(0, 33), (40, 70), (0, 1), (100, 130)]
+    print(f"prefill scale={scale}", flush=True)
+    q, kc, vc, bt, qsl, lens = prefill_case(chunks, 8, 2, 128, torch.bfloat16, seed=5)
+    out = run_prefill(q, kc, vc, bt, qsl, lens, scale)
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, scale, dtype_name(q))
+    assert_close(out, want, what=f"prefill scale={scale}")
+
+
 def test_prefill_chunking_and_decode_agree():
     """Rows computed as one chunk, as two chunks, and the last row as a
     decode step all agree within tolerance of the oracle."""
