@@ -36,6 +36,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,7 +49,7 @@ constexpr int kBlock = 16;
 constexpr int kTileKeys = 64;                      // keys per LDS stage
 constexpr int kTileBlocks = kTileKeys / kBlock;
 
-template <int D>
+template <class T, int D>
 struct PrefillLds {
   static constexpr int kRow = D * 2 + 16;          // bytes per K row (one key)
   static constexpr int kVRow = kBlock * 2 + 16;    // bytes per V row (one dim of a block)
@@ -55,6 +57,8 @@ struct PrefillLds {
   static constexpr int kBytesVBlock = D * kVRow;
   static constexpr int kBytes = kBytesK + kTileBlocks * kBytesVBlock;
 };
+
+template <class X> struct TypeTag { using type = X; };
 
 // Position of key r (0..31) of a 32-key half in LDS: bits 2 and 3 swapped.
 __device__ __forceinline__ int swap_bits23(int r) {
@@ -68,7 +72,7 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 template <class T, int D>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
-  using Lds = PrefillLds<D>;
+  using Lds = PrefillLds<T, D>;
   constexpr int KS = D / 16;                 // QK^T k-steps
   constexpr int DT = D / 32;                 // 32-dim output tiles
   constexpr int UPB = 2 * D;                 // 16-byte units per block per tensor
@@ -159,7 +163,7 @@ void prefill_kernel(PrefillArgs a) {
   // that the loads are unconditional and each wait covers only its own set.
   u32x4 pk0[UPT], pv0[UPT], pk1[UPT], pv1[UPT];
   bool bad_id = false;
-  auto fetch = [&](u32x4 (&pk)[UPT], u32x4 (&pv)[UPT], int t) {
+  auto fetch = [&](u32x4 (&pk)[UPT], u32x4 (&pv)[UPT], int t) __attribute__((always_inline)) {
     t = min(t, n_tiles - 1);
 #pragma unroll
     for (int r = 0; r < UPT; ++r) {
@@ -182,8 +186,13 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
   // Registers -> LDS.  V slots past the sequence end are zeroed (they may
-  // hold stale data, and 0 * NaN would leak into P.V).
-  auto stash = [&](const u32x4 (&pk)[UPT], const u32x4 (&pv)[UPT], int t) {
+  // hold stale data, and 0 * NaN would leak into P.V).  With kHalf the V
+  // tile is stored as fp16: bf16 -> fp16 is exact for magnitudes up to 65504
+  // (8 significant bits fit in 11) and loses at most 2^-24 in absolute terms
+  // below fp16's normal range; a larger or non-finite value sets `wide`.
+  auto stash = [&](auto half_tag, const u32x4 (&pk)[UPT], const u32x4 (&pv)[UPT], int t,
+                   bool& wide) __attribute__((always_inline)) {
+    constexpr bool kHalf = decltype(half_tag)::value;
 #pragma unroll
     for (int r = 0; r < UPT; ++r) {
       const int u = r * kPrefillThreads + tid;
@@ -208,6 +217,19 @@ void prefill_kernel(PrefillArgs a) {
           v[e] = x;
         }
       }
+      if constexpr (kHalf) {
+        uint32_t mag = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = v[e];
+          const uint32_t ax = x & 0x7fff7fffu;
+          mag = max(mag, max(ax & 0xffffu, ax >> 16));
+          const auto h2 = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, x << 16),
+                                                     __builtin_bit_cast(float, x & 0xffff0000u));
+          v[e] = __builtin_bit_cast(uint32_t, h2);
+        }
+        wide |= mag > 0x477fu;                // bf16 bits of 65280, the largest below 65504
+      }
       *reinterpret_cast<u32x4*>(lds + Lds::kBytesK + b * Lds::kBytesVBlock + dim * Lds::kVRow + h16 * 16) = v;
     }
   };
@@ -220,7 +242,7 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
 
   // One key tile: S^T, online softmax, P.V, all from LDS.
-  auto compute = [&](int t) {
+  auto compute = [&](auto half_tag, int t) __attribute__((always_inline)) {
     const int k0 = t * kTileKeys;
     if (!wave_on || k0 > wave_lim) return;
 
@@ -274,43 +296,55 @@ void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
     const float neg_m = -m_run;
-    // The row sum adds the unrounded weights.  bf16 weights enter P.V as
-    // hi + lo halves that reproduce each weight to about 2^-17, and fp16
-    // weights to 2^-12, so the normalisation stays consistent with P.V to far
-    // below the output's own rounding.
-    float psum = 0.f;
-    u32x4 pB[4], pBl[4];             // P^T operands of the four 16-key k-steps
+    // One P.V pass in element type P from the V copy at vbase.  kPart 0
+    // enters each weight whole, 1 its leading half (its type's rounding of
+    // it), 2 the remainder; passes 0 and 1 add the unrounded weights to the
+    // row sum.  fp16 weights alone are good to 2^-12 and bf16 hi + lo to
+    // about 2^-17, so either way the normalisation stays consistent with P.V
+    // to far below the output's own rounding.  Splitting into two passes
+    // (recomputing the exponentials) keeps one set of P operands live.
+    auto pv_pass = [&](auto ptag, auto part, const unsigned char* vbase) __attribute__((always_inline)) {
+      using P = typename decltype(ptag)::type;
+      constexpr int kPart = decltype(part)::value;
+      float psum = 0.f;
+      u32x4 pB[4];                     // P^T operands of the four 16-key k-steps
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        uint16_t hi[8], lo[8];
+        for (int cc = 0; cc < 2; ++cc) {
+          uint16_t w16[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pe = fast_exp2(fmaf(s[c2][8 * cc + j], c_log2, neg_m));   // masked: -inf
-          hi[j] = from_f32<T>(pe);
-          if constexpr (SplitP<T>::kSplit) {
-            lo[j] = from_f32<T>(pe - to_f32<T>(hi[j]));
-          } else {
-            lo[j] = 0;
+          for (int j = 0; j < 8; ++j) {
+            const float pe = fast_exp2(fmaf(s[c2][8 * cc + j], c_log2, neg_m));   // masked: -inf
+            const uint16_t h = from_f32<P>(pe);
+            w16[j] = kPart == 2 ? from_f32<P>(pe - to_f32<P>(h)) : h;
+            if constexpr (kPart != 2) psum += pe;
           }
-          psum += pe;
+          pB[2 * c2 + cc] = u32x4{pack2(w16[0], w16[1]), pack2(w16[2], w16[3]), pack2(w16[4], w16[5]), pack2(w16[6], w16[7])};
         }
-        pB[2 * c2 + cc] = u32x4{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
-        pBl[2 * c2 + cc] = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
-      }
-    l_run += psum;
+      if constexpr (kPart != 2) l_run += psum;
 
-    // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys 8*half .. +7.
+      // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys 8*half .. +7.
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const unsigned char* vr = lds + Lds::kBytesK + kk * Lds::kBytesVBlock + r32 * Lds::kVRow + 16 * half;
+      for (int kk = 0; kk < 4; ++kk) {
+        const unsigned char* vr = vbase + kk * Lds::kBytesVBlock + r32 * Lds::kVRow + 16 * half;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 vA = *reinterpret_cast<const u32x4*>(vr + 32 * dt * Lds::kVRow);
-        o[dt] = mfma32x32x16<T>(vA, pB[kk], o[dt]);
-        if constexpr (SplitP<T>::kSplit) o[dt] = mfma32x32x16<T>(vA, pBl[kk], o[dt]);
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x4 vA = *reinterpret_cast<const u32x4*>(vr + 32 * dt * Lds::kVRow);
+          o[dt] = mfma32x32x16<P>(vA, pB[kk], o[dt]);
+        }
       }
+    };
+    using Part0 = std::integral_constant<int, 0>;
+    using Part1 = std::integral_constant<int, 1>;
+    using Part2 = std::integral_constant<int, 2>;
+    if constexpr (decltype(half_tag)::value) {
+      pv_pass(TypeTag<F16>{}, Part0{}, lds + Lds::kBytesK);
+    } else if constexpr (SplitP<T>::kSplit) {
+      pv_pass(TypeTag<T>{}, Part1{}, lds + Lds::kBytesK);
+      pv_pass(TypeTag<T>{}, Part2{}, lds + Lds::kBytesK);
+    } else {
+      pv_pass(TypeTag<T>{}, Part0{}, lds + Lds::kBytesK);
     }
   };
 
@@ -318,24 +352,52 @@ void prefill_kernel(PrefillArgs a) {
   // bottom (an odd count gets one more, fully masked tile whose compute
   // returns at once): a break between the two halves would merge a path on
   // which set 1 was never loaded into the loop header and force every wait
-  // there to drain all loads.
-  fetch(pk0, pv0, 0);
-  __builtin_amdgcn_sched_barrier(0);   // keep set 0's loads older than set 1's
-  fetch(pk1, pv1, 1);
-  int t = 0;
-  do {
-    __syncthreads();                 // every wave is done with the previous tile
-    stash(pk0, pv0, t);
-    __syncthreads();                 // tile t is in LDS
-    fetch(pk0, pv0, t + 2);
-    compute(t);
-    __syncthreads();
-    stash(pk1, pv1, t + 1);
-    __syncthreads();
-    fetch(pk1, pv1, t + 3);
-    compute(t + 1);
-    t += 2;
-  } while (t < n_tiles);
+  // there to drain all loads.  With kHalf (bf16 data, V as fp16) the pass
+  // gives up as soon as a tile is wide and returns false.
+  auto run = [&](auto half_tag) __attribute__((always_inline)) -> bool {
+    constexpr bool kHalf = decltype(half_tag)::value;
+    fetch(pk0, pv0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep set 0's loads older than set 1's
+    fetch(pk1, pv1, 1);
+    int t = 0;
+    do {
+      bool wide = false;
+      __syncthreads();                 // every wave is done with the previous tile
+      stash(half_tag, pk0, pv0, t, wide);
+      if constexpr (kHalf) {
+        if (__syncthreads_or(wide)) return false;   // tile t is in LDS
+      } else {
+        __syncthreads();
+      }
+      fetch(pk0, pv0, t + 2);
+      compute(half_tag, t);
+      __syncthreads();
+      stash(half_tag, pk1, pv1, t + 1, wide);
+      if constexpr (kHalf) {
+        if (__syncthreads_or(wide)) return false;
+      } else {
+        __syncthreads();
+      }
+      fetch(pk1, pv1, t + 3);
+      compute(half_tag, t + 1);
+      t += 2;
+    } while (t < n_tiles);
+    return true;
+  };
+  // bf16 data first tries the fp16 P.V (one product per weight); a workgroup
+  // that meets a V value beyond fp16's range starts over with split bf16
+  // weights (two products per weight).
+  bool done = false;
+  if constexpr (std::is_same<T, BF16>::value) done = run(std::true_type{});
+  if (!done) {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    run(std::false_type{});
+  }
 
   const bool poison = __syncthreads_or(bad_id);
   l_run += __shfl_xor(l_run, 32);

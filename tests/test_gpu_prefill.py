@@ -90,6 +90,22 @@ def test_prefill_scale_sign_and_size(scale):
     assert_close(out, want, what=f"prefill scale={scale}")
 
 
+def test_prefill_bf16_values_beyond_fp16_range():
+    """bf16 V values the fp16 P.V cannot hold (2e5) in one sequence, and the
+    largest bf16 value it can (65280) in another: both match the oracle."""
+    chunks = [(40, 90), (300, 70)]
+    print("prefill wide bf16 values", flush=True)
+    q, kc, vc, bt, qsl, lens = prefill_case(chunks, 8, 2, 128, torch.bfloat16, seed=8)
+    for c, val in ((0, 2.0e5), (1, 65280.0)):
+        for pos in (3, 57, int(lens[c]) - 2):
+            blk = int(bt[c, pos // 16])
+            vc[blk, :, 5:9, pos % 16] = val
+            vc[blk, :, 100, pos % 16] = -val
+    out = run_prefill(q, kc, vc, bt, qsl, lens, 0.088)
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, 0.088, dtype_name(q))
+    assert_close(out, want, what="prefill wide values")
+
+
 def test_prefill_chunking_and_decode_agree():
     """Rows computed as one chunk, as two chunks, and the last row as a
     decode step all agree within tolerance of the oracle."""
