@@ -67,6 +67,10 @@ __device__ __forceinline__ int swap_bits23(int r) {
 
 constexpr int kPrefillWaves = 8;
 constexpr float kLazyLog2 = 8.f;      // running-maximum slack, log2 units
+#ifndef PF_PREFETCH
+#define PF_PREFETCH 4
+#endif
+constexpr int kPrefetch = PF_PREFETCH;   // LDS operand reads in flight ahead of the MFMAs
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
 template <class T, int D>
@@ -246,16 +250,30 @@ void prefill_kernel(PrefillArgs a) {
     const int k0 = t * kTileKeys;
     if (!wave_on || k0 > wave_lim) return;
 
-    // S^T for the two 32-key halves of the tile.
+    // S^T for the two 32-key halves of the tile, their k-steps alternating
+    // (two independent accumulation chains).  Operand j is read from LDS
+    // kPrefetch products ahead of its use, and the scheduling fences keep
+    // the compiler from sinking the reads next to their uses.
     f32x16 s[2];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[c2][i] = 0.f;
-      const unsigned char* kr = lds + (32 * c2 + r32) * Lds::kRow + 16 * half;
+    {
+      const unsigned char* kr = lds + r32 * Lds::kRow + 16 * half;
+      auto kop = [&](int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4*>(kr + (j & 1) * 32 * Lds::kRow + 32 * (j >> 1));
+      };
+      u32x4 kb[kPrefetch];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[c2] = mfma32x32x16<T>(*reinterpret_cast<const u32x4*>(kr + 32 * ks), qb[ks], s[c2]);
+      for (int j = 0; j < kPrefetch; ++j) kb[j] = kop(j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2 * KS; ++j) {
+        s[j & 1] = mfma32x32x16<T>(kb[j % kPrefetch], qb[j >> 1], s[j & 1]);
+        if (j + kPrefetch < 2 * KS) kb[j % kPrefetch] = kop(j + kPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // Element i of half c2 in this lane is key k0 + 32*c2 + 16*(i/8) + 8*half + i%8.
@@ -324,15 +342,22 @@ void prefill_kernel(PrefillArgs a) {
         }
       if constexpr (kPart != 2) l_run += psum;
 
-      // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys 8*half .. +7.
+      // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys
+      // 8*half .. +7.  Product j = (kk, dt) = (j / DT, j % DT); operands are
+      // read kPrefetch products ahead, as for S^T.
+      const unsigned char* vr = vbase + r32 * Lds::kVRow + 16 * half;
+      auto vop = [&](int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4*>(vr + (j / DT) * Lds::kBytesVBlock + 32 * (j % DT) * Lds::kVRow);
+      };
+      u32x4 vb[kPrefetch];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const unsigned char* vr = vbase + kk * Lds::kBytesVBlock + r32 * Lds::kVRow + 16 * half;
+      for (int j = 0; j < kPrefetch; ++j) vb[j] = vop(j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const u32x4 vA = *reinterpret_cast<const u32x4*>(vr + 32 * dt * Lds::kVRow);
-          o[dt] = mfma32x32x16<P>(vA, pB[kk], o[dt]);
-        }
+      for (int j = 0; j < 4 * DT; ++j) {
+        o[j % DT] = mfma32x32x16<P>(vb[j % kPrefetch], pB[j / DT], o[j % DT]);
+        if (j + kPrefetch < 4 * DT) vb[j % kPrefetch] = vop(j + kPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     using Part0 = std::integral_constant<int, 0>;
