@@ -59,6 +59,7 @@ struct PrefillLds {
 };
 
 template <class X> struct TypeTag { using type = X; };
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Position of key r (0..31) of a 32-key half in LDS: bits 2 and 3 swapped.
 __device__ __forceinline__ int swap_bits23(int r) {
@@ -222,17 +223,17 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
       if constexpr (kHalf) {
-        uint32_t mag = 0;
+        // Largest magnitude of each 16-bit half, one packed integer max per dword.
+        u16x2 mag = {0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t x = v[e];
-          const uint32_t ax = x & 0x7fff7fffu;
-          mag = max(mag, max(ax & 0xffffu, ax >> 16));
+          mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, x & 0x7fff7fffu));
           const auto h2 = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, x << 16),
                                                      __builtin_bit_cast(float, x & 0xffff0000u));
           v[e] = __builtin_bit_cast(uint32_t, h2);
         }
-        wide |= mag > 0x477fu;                // bf16 bits of 65280, the largest below 65504
+        wide |= max(mag[0], mag[1]) > 0x477f;   // bf16 bits of 65280, the largest below 65504
       }
       *reinterpret_cast<u32x4*>(lds + Lds::kBytesK + b * Lds::kBytesVBlock + dim * Lds::kVRow + h16 * 16) = v;
     }
