@@ -241,3 +241,156 @@ def test_random_operations_keep_invariants(ops, seed):
     for s in seqs:
         p.seq_free(s)
     assert p.num_free() == 24
+
+
+# ---------------------------------------------------------------------------
+# prefix caching: ground truth is what each physical slot actually holds
+# ---------------------------------------------------------------------------
+
+class SlotTruth:
+    """What a device cache would hold, slot by slot: the full token prefix
+    of the token written there (unknown tokens get a unique marker).  Hits
+    are correct only if the reused slots hold exactly the sequence's own
+    prefix; copy-on-write pairs copy whole blocks, as the device does."""
+
+    def __init__(self, B):
+        self.B = B
+        self.slot = {}
+        self.prefix = {}
+        self.unknown = 0
+
+    def create(self, sid):
+        self.prefix[sid] = ()
+
+    def fork(self, parent, child):
+        self.prefix[child] = self.prefix[parent]
+
+    def apply(self, m, sid, tokens, slots, cow, n_hit):
+        for src, dst in cow:
+            for o in range(self.B):
+                if src * self.B + o in self.slot:
+                    self.slot[dst * self.B + o] = self.slot[src * self.B + o]
+        table, _ = m.block_table(sid)
+        base = len(self.prefix[sid])
+        for i, t in enumerate(tokens):
+            if t is None:
+                self.unknown += 1
+                t = ("unknown", self.unknown)
+            self.prefix[sid] = self.prefix[sid] + (t,)
+            pos = base + i
+            phys = table[pos // self.B] * self.B + pos % self.B
+            if i < n_hit:
+                assert slots[i] == -1
+                assert self.slot.get(phys) == self.prefix[sid], "reused slot holds other content"
+            else:
+                assert slots[i] == phys
+                self.slot[phys] = self.prefix[sid]
+
+
+def _check_pool_invariants(m):
+    live = {}
+    for sid, tab in m.tables.items():
+        for b in tab:
+            live[b] = live.get(b, 0) + 1
+    assert m.num_free() + m.num_cached() + len(live) == m.N
+    for b in range(m.N):
+        assert m.ref[b] == live.get(b, 0)
+    for b in m.evictable:
+        assert m.ref[b] == 0 and m.content_of_block[b] >= 0
+    assert len(set(m.stack) | set(m.evictable)) == len(m.stack) + len(m.evictable)
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.integers(0, 4), st.integers(0, 40), st.integers(0, 7), st.integers(0, 3)),
+                min_size=1, max_size=60),
+       st.integers(0, 2 ** 64 - 1))
+def test_prefix_cache_reuses_only_identical_content(ops, seed):
+    B, N = 4, 40
+    m = PoolModel(N, B, seed, prefix_caching=True)
+    truth = SlotTruth(B)
+    seqs = []
+    # A few shared "prompts": tokens come from them so that prefixes repeat.
+    prompts = [[1, 2, 3, 4] * 10, [1, 2, 3, 4, 9, 9, 9, 9] * 5, [5] * 40, list(range(40))]
+    for op, n, pick, which in ops:
+        if op == 0 or not seqs:
+            sid = m.seq_create()
+            truth.create(sid)
+            seqs.append(sid)
+        elif op == 1:
+            parent = seqs[pick % len(seqs)]
+            sid = m.seq_fork(parent)
+            truth.fork(parent, sid)
+            seqs.append(sid)
+        elif op in (2, 3):
+            sid = seqs[pick % len(seqs)]
+            k = m.ntok[sid]
+            src = prompts[which]
+            tokens = [src[(k + i) % len(src)] for i in range(n)] if op == 2 else [None] * n
+            try:
+                if op == 2:
+                    slots, cow, n_hit = m.seq_append_tokens(sid, tokens, n - 1)
+                else:
+                    slots, cow = m.seq_append(sid, n)
+                    n_hit = 0
+            except PoolError as e:
+                assert e.code == "ENOMEM"
+            else:
+                assert n_hit % B == 0 and n_hit <= max(0, n - 1)
+                truth.apply(m, sid, tokens, slots, cow, n_hit)
+        else:
+            sid = seqs.pop(pick % len(seqs))
+            m.seq_free(sid)
+        _check_pool_invariants(m)
+
+
+def test_prefix_cache_hand_traced():
+    """Two requests with one 3-block prompt, the first freed before the
+    second arrives: the second reuses all three blocks (keeping its last
+    token to compute), and eviction hands cached blocks out only after the
+    free stack is empty, least recently released first."""
+    B = 4
+    m = PoolModel(12, B, 0, prefix_caching=True)
+    prompt = list(range(100, 113))              # 13 tokens: 3 full blocks + 1
+    a = m.seq_create()
+    slots, cow, hit = m.seq_append_tokens(a, prompt, len(prompt) - 1)
+    assert hit == 0 and cow == [] and slots == list(range(13))
+    assert m.block_table(a) == ([0, 1, 2, 3], 13)
+    m.seq_free(a)
+    # blocks 0..2 are registered (full), block 3 is not: it goes back on the stack
+    assert m.num_cached() == 3 and m.evictable == [0, 1, 2] and m.stack[-1] == 3
+    b = m.seq_create()
+    slots, cow, hit = m.seq_append_tokens(b, prompt, len(prompt) - 1)
+    assert hit == 12 and slots[:12] == [-1] * 12 and slots[12] == 3 * B
+    assert m.block_table(b) == ([0, 1, 2, 3], 13) and m.num_cached() == 0
+    # max_hit_tokens short of a whole block: only two blocks reused
+    c = m.seq_create()
+    slots, cow, hit = m.seq_append_tokens(c, prompt, 11)
+    assert hit == 8 and m.block_table(c)[0][:2] == [0, 1] and m.refcount(0) == 2
+    # a different token in block 1 breaks the chain from there on
+    d = m.seq_create()
+    other = prompt[:5] + [7] + prompt[6:]
+    _, _, hit = m.seq_append_tokens(d, other, 100)
+    assert hit == 4
+    for s in (b, c, d):
+        m.seq_free(s)
+    _check_pool_invariants(m)
+    # Everything released; allocation drains the stack, then evicts LRU-first.
+    cached = list(m.evictable)
+    e = m.seq_create()
+    m.seq_append(e, B * (m.num_free() + 1))
+    assert m.block_table(e)[0][-1] == cached[0]
+    assert cached[0] not in m.block_of_content.values()
+
+
+def test_prefix_cache_off_is_the_plain_pool():
+    for seed in (0, 3):
+        a, b = PoolModel(20, 4, seed), PoolModel(20, 4, seed, prefix_caching=False)
+        for m in (a, b):
+            s = m.seq_create()
+            m.seq_append(s, 9)
+            t = m.seq_create()
+            m.seq_append_tokens(t, [1] * 9, 8)
+            m.seq_free(s)
+            u = m.seq_create()
+            assert m.seq_append_tokens(u, [1] * 9, 8)[2] == 0    # no hits without caching
+        assert a.stack == b.stack and a.tables == b.tables and a.num_cached() == 0
