@@ -20,15 +20,18 @@ same workload on this host's cores.
 
 Other workloads (--workload): llama8b_gqa, llama13b_shared (prefix sharing
 built through the block pool), mixed (slot-mapped write + 2 prefill chunks +
-4096 decode sequences, each call timed), tiny, and prefill (the mixed step's
-slot-mapped write and two 2048-row chunks alone, without its decode batch:
-the MFMA-bound part, reported against the matrix-core roofline).
+4096 decode sequences, each call timed), tiny, prefill (the mixed step's
+two 2048-row chunks alone, without its decode batch: the MFMA-bound part,
+reported against the matrix-core roofline), and prefix_cache (a RAG-shaped
+batch of 32 requests sharing one 1024-token document, written and prefilled
+with and without automatic prefix caching).
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -51,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill"])
+                    choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill",
+                             "prefix_cache"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's own, 0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -215,6 +219,94 @@ def build_shared_cache(torch, pa, w, k_tok, v_tok):
     return kc, vc, bt, ctx, used
 
 
+def bench_prefix_cache(args, np, torch, pa):
+    """RAG-shaped batch: R requests = one shared 1024-token document + a
+    unique 256-token query each, 8B-GQA shape, bf16.  A request served
+    earlier left the document's blocks in the cache (untimed set-up), so with
+    prefix caching each request writes and prefills only its 256 new tokens
+    over 1024 cached keys; without it, all 1280.  A step = pa_write_kv of the
+    batch's new tokens + pa_prefill_chunk of its chunks; host admission
+    (pool calls) is timed separately."""
+    R, DOC, QRY, Hq, Hkv, D, B = 32, 1024, 256, 32, 8, 128, 16
+    L = DOC + QRY
+    rng = np.random.Generator(np.random.PCG64(4230))
+    doc = rng.integers(0, 32000, DOC).tolist()
+    queries = [rng.integers(0, 32000, QRY).tolist() for _ in range(R + 1)]
+    num_blocks = int(1.2 * (R + 1) * (L // B))
+    g = torch.Generator(device="cuda").manual_seed(4230)
+    dt = torch.bfloat16
+    kc = torch.randn(num_blocks, Hkv, B, D, generator=g, device="cuda").to(dt)
+    vc = torch.randn(num_blocks, Hkv, D, B, generator=g, device="cuda").to(dt)
+
+    def admit(caching):
+        pool = pa.BlockPool(num_blocks, B, 4230, prefix_caching=caching)
+        warm = pool.create()
+        pool.append_tokens(warm, doc + queries[R], L - 1)
+        pool.free(warm)
+        t0 = time.perf_counter()
+        seqs, slots, hits = [], [], []
+        for r in range(R):
+            sid = pool.create()
+            sl, cow, hit = pool.append_tokens(sid, doc + queries[r], L - 1)
+            seqs.append(sid)
+            slots += sl[hit:]
+            hits.append(hit)
+        tabs, ctx = pool.block_tables(seqs, stride=L // B)
+        host_us = (time.perf_counter() - t0) * 1e6 / R
+        return tabs, ctx, np.array(slots, np.int64), hits, host_us
+
+    def prefill_flop(n_cached, n):
+        return Hq * 4 * D * (n * n_cached + n * (n + 1) // 2)
+
+    results = {}
+    for caching in (True, False):
+        tabs, ctx, slots, hits, host_us = admit(caching)
+        host = [admit(caching)[4] for _ in range(5)]
+        n_new = [L - h for h in hits]
+        T = sum(n_new)
+        k_new = torch.randn(T, Hkv, D, generator=g, device="cuda").to(dt)
+        v_new = torch.randn(T, Hkv, D, generator=g, device="cuda").to(dt)
+        q = torch.randn(T, Hq, D, generator=g, device="cuda").to(dt)
+        out = torch.empty_like(q)
+        sm = torch.from_numpy(slots).cuda()
+        bt = torch.from_numpy(tabs).cuda()
+        qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).cuda()
+        sl_t = torch.from_numpy(ctx).cuda()
+        scale = 1.0 / math.sqrt(D)
+        fns = [lambda: pa.write_kv(k_new, v_new, kc, vc, sm),
+               lambda: pa.prefill_chunk(out, q, kc, vc, bt, qsl, sl_t, max(n_new), L, scale)]
+        timer = StepTimer(torch, evict=not args.warm_cache)
+        timer.run(args.warmup, fns)
+        per, total, wall = timer.run(args.steps, fns)
+        flop = sum(prefill_flop(h, n) for h, n in zip(hits, n_new))
+        results[caching] = {
+            "us_per_step": round(mean(total) * 1e3, 2), "write_kv_us": round(mean(per[0]) * 1e3, 2),
+            "prefill_us": round(mean(per[1]) * 1e3, 2), "new_tokens": T, "cached_tokens": sum(hits),
+            "prefill_flop": int(flop), "prefill_tflops": round(flop / (mean(per[1]) * 1e-3) / 1e12, 1),
+            "host_admit_us_per_request": round(float(np.median(host)), 2), "wall_ms_per_step": round(wall, 5)}
+    on, off = results[True], results[False]
+    tflops = on["prefill_tflops"]
+    line = {
+        "metric": "prefill step time of a RAG-shaped batch with automatic prefix caching",
+        "value": on["us_per_step"], "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(on["us_per_step"] / 1e3, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefix_cache: {R} requests of one shared {DOC}-token document + a unique "
+                               f"{QRY}-token query, {Hq} query heads over {Hkv} KV heads, head_dim {D}, bf16; "
+                               "step = slot-mapped write of the new tokens + chunked prefill",
+                   "cache": "warm" if args.warm_cache else "Infinity Cache evicted before each step",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_16BIT_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_16BIT_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "pa_prefill_chunk (prefill_kernel), cached prefix"},
+        "with_prefix_cache": on, "without_prefix_cache": off,
+        "speedup": round(off["us_per_step"] / on["us_per_step"], 2),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -234,6 +326,8 @@ def main():
     if args.copy_calibration:
         return copy_calibration(torch)
     name = args.workload
+    if name == "prefix_cache":
+        return bench_prefix_cache(args, np, torch, pa)
     w = W.mixed(num_decode=0) if name == "prefill" else W.make_workload(name)
     timer = StepTimer(torch, evict=not args.warm_cache)
     extra = {}

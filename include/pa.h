@@ -183,6 +183,32 @@ typedef struct pa_pool pa_pool;
 
 pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed,
                          pa_pool** out);
+
+/* Prefix caching ("Inside vLLM ...", section "PagedAttention in a Python RAG
+ * Application" and its question on how prefix caching works; "PagedAttention
+ * in vLLM: A Throughput Settings Guide", section "Tuning Batching, Prefill,
+ * and Cache"): the content of each full block is keyed, and a request whose
+ * leading whole blocks match content already computed reuses those physical
+ * blocks instead of recomputing them.
+ *   - A block's content is its token ids and everything before them: its key
+ *     is (the content of the block before it, its token ids), compared
+ *     exactly (the hash only indexes the table).
+ *   - A block is registered when its last slot is appended through
+ *     pa_seq_append_tokens, if the block before it is registered (or it is
+ *     the sequence's first block).  Tokens appended by pa_seq_append have no
+ *     ids, so their blocks are never registered.
+ *   - When a registered block's references drop to zero it is not freed: it
+ *     goes to the tail of an LRU list of cached blocks (pa_pool_num_cached).
+ *     A later match takes it back; allocation uses the free stack first and
+ *     only then evicts the head of that list, which forgets its content.
+ * Without PA_POOL_PREFIX_CACHING the pool behaves exactly as pa_pool_create's
+ * (and pa_seq_append_tokens never reuses). */
+#define PA_POOL_PREFIX_CACHING 1u
+/* flags: 0 or PA_POOL_PREFIX_CACHING; other bits give PA_EINVAL. */
+pa_status pa_pool_create_ex(int32_t num_blocks, int32_t block_size, uint64_t seed,
+                            uint32_t flags, pa_pool** out);
+/* Cached blocks (no references, content kept); -1 if pool is NULL. */
+int32_t   pa_pool_num_cached(const pa_pool* pool);
 void      pa_pool_destroy(pa_pool* pool);                 /* NULL-safe */
 int32_t   pa_pool_num_free(const pa_pool* pool);          /* -1 if pool is NULL */
 int32_t   pa_pool_num_blocks(const pa_pool* pool);        /* -1 if pool is NULL */
@@ -202,8 +228,22 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t* child);
 pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens,
                         int64_t* slot_mapping_out, int32_t* cow_pairs_out,
                         int32_t cow_cap, int32_t* n_cow);
+/* pa_seq_append with the tokens' ids (token_ids[n_tokens], host).  With
+ * prefix caching, when the sequence ends on a block boundary, the longest run
+ * of leading whole blocks of the new tokens (at most max_hit_tokens tokens)
+ * whose content is cached is reused: those blocks join the table (one more
+ * reference each), their tokens get slot -1 (their K/V is already stored;
+ * pa_write_kv skips them) and *n_hit counts them.  The rest is appended as by
+ * pa_seq_append.  Callers that must compute the last token pass
+ * max_hit_tokens = n_tokens - 1.  All-or-nothing over the free stack plus the
+ * cached blocks, less the cached blocks this call reuses. */
+pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq, const int32_t* token_ids,
+                               int32_t n_tokens, int32_t max_hit_tokens,
+                               int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                               int32_t cow_cap, int32_t* n_cow, int32_t* n_hit);
 /* Drop one reference from every block of seq, in table order; blocks that
- * reach zero go back on the free stack in that order. */
+ * reach zero go back on the free stack in that order (registered blocks, with
+ * prefix caching, to the tail of the cached list instead). */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq);
 /* Block table of one sequence: up to cap ids into out (host). */
 pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap,

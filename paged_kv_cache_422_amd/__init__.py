@@ -30,6 +30,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_ENOTSUP = range(5)
+PA_POOL_PREFIX_CACHING = 1          # pa_pool_create_ex flag
 PA_FP16, PA_BF16 = 0, 1
 _STATUS = {1: "EINVAL", 2: "ENOMEM", 3: "EHIP", 4: "ENOTSUP"}
 
@@ -52,6 +53,8 @@ _SIGS = {
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "pa_pool_create": (c_i32, [c_i32, c_i32, c_u64, ctypes.POINTER(c_vp)]),
+    "pa_pool_create_ex": (c_i32, [c_i32, c_i32, c_u64, ctypes.c_uint32, ctypes.POINTER(c_vp)]),
+    "pa_pool_num_cached": (c_i32, [c_vp]),
     "pa_pool_destroy": (None, [c_vp]),
     "pa_pool_num_free": (c_i32, [c_vp]),
     "pa_pool_num_blocks": (c_i32, [c_vp]),
@@ -59,6 +62,8 @@ _SIGS = {
     "pa_seq_create": (c_i32, [c_vp, P_i64]),
     "pa_seq_fork": (c_i32, [c_vp, c_i64, P_i64]),
     "pa_seq_append": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, c_i32, P_i32]),
+    "pa_seq_append_tokens": (c_i32, [c_vp, c_i64, P_i32, c_i32, c_i32, P_i64, P_i32, c_i32, P_i32,
+                                     P_i32]),
     "pa_seq_free": (c_i32, [c_vp, c_i64]),
     "pa_seq_block_table": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32, P_i32]),
     "pa_seq_block_tables": (c_i32, [c_vp, P_i64, c_i32, P_i32, c_i32, c_i32, P_i32]),
@@ -181,14 +186,17 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, q_start_loc, seq_lens,
 class BlockPool:
     """Refcounted block pool with copy-on-write (host side, ids only)."""
 
-    def __init__(self, num_blocks: int, block_size: int = 16, seed: int = 0):
+    def __init__(self, num_blocks: int, block_size: int = 16, seed: int = 0,
+                 prefix_caching: bool = False):
         h = c_vp()
-        _check(_lib.pa_pool_create(num_blocks, block_size, seed, ctypes.byref(h)))
+        flags = PA_POOL_PREFIX_CACHING if prefix_caching else 0
+        _check(_lib.pa_pool_create_ex(num_blocks, block_size, seed, flags, ctypes.byref(h)))
         self._h = h
         self.block_size = block_size
 
     def close(self):
-        if getattr(self, "_h", None):
+        # At interpreter exit the module globals may already be gone.
+        if getattr(self, "_h", None) and _lib is not None:
             _lib.pa_pool_destroy(self._h)
             self._h = None
 
@@ -202,6 +210,10 @@ class BlockPool:
     @property
     def num_blocks(self) -> int:
         return int(_lib.pa_pool_num_blocks(self._h))
+
+    @property
+    def num_cached(self) -> int:
+        return int(_lib.pa_pool_num_cached(self._h))
 
     def refcount(self, block: int) -> int:
         return int(_lib.pa_block_refcount(self._h, block))
@@ -223,6 +235,18 @@ class BlockPool:
         n_cow = c_i32(0)
         _check(_lib.pa_seq_append(self._h, seq, n_tokens, slots, cow, 1, ctypes.byref(n_cow)))
         return list(slots[:n_tokens]), ([(cow[0], cow[1])] if n_cow.value else [])
+
+    def append_tokens(self, seq: int, tokens, max_hit_tokens: int):
+        """Returns (slots, cow, n_hit); the first n_hit tokens reuse cached
+        blocks and have slot -1."""
+        n = len(tokens)
+        ids = (c_i32 * max(n, 1))(*[int(t) for t in tokens])
+        slots = (c_i64 * max(n, 1))()
+        cow = (c_i32 * 2)()
+        n_cow, n_hit = c_i32(0), c_i32(0)
+        _check(_lib.pa_seq_append_tokens(self._h, seq, ids, n, max_hit_tokens, slots, cow, 1,
+                                         ctypes.byref(n_cow), ctypes.byref(n_hit)))
+        return list(slots[:n]), ([(cow[0], cow[1])] if n_cow.value else []), n_hit.value
 
     def free(self, seq: int):
         _check(_lib.pa_seq_free(self._h, seq))

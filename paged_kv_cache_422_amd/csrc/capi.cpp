@@ -18,7 +18,7 @@
 
 struct pa_pool {
   pa::BlockPool impl;
-  pa_pool(int32_t n, int32_t b, uint64_t seed) : impl(n, b, seed) {}
+  pa_pool(int32_t n, int32_t b, uint64_t seed, bool caching) : impl(n, b, seed, caching) {}
 };
 
 namespace {
@@ -273,15 +273,22 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
 // host block pool
 // ---------------------------------------------------------------------------
 
-pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed, pa_pool** out) {
+pa_status pa_pool_create_ex(int32_t num_blocks, int32_t block_size, uint64_t seed, uint32_t flags,
+                            pa_pool** out) {
   if (!out) return fail(PA_EINVAL, "pa_pool_create: out is null");
   *out = nullptr;
   if (num_blocks <= 0 || block_size <= 0)
     return fail(PA_EINVAL, "pa_pool_create: num_blocks and block_size must be positive");
-  pa_pool* p = new (std::nothrow) pa_pool(num_blocks, block_size, seed);
+  if (flags & ~static_cast<uint32_t>(PA_POOL_PREFIX_CACHING))
+    return fail(PA_EINVAL, "pa_pool_create_ex: unknown flags");
+  pa_pool* p = new (std::nothrow) pa_pool(num_blocks, block_size, seed, (flags & PA_POOL_PREFIX_CACHING) != 0);
   if (!p) return fail(PA_ENOMEM, "pa_pool_create: host allocation failed");
   *out = p;
   return ok();
+}
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed, pa_pool** out) {
+  return pa_pool_create_ex(num_blocks, block_size, seed, 0, out);
 }
 
 void pa_pool_destroy(pa_pool* pool) { delete pool; }
@@ -289,6 +296,8 @@ void pa_pool_destroy(pa_pool* pool) { delete pool; }
 int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->impl.num_free() : -1; }
 
 int32_t pa_pool_num_blocks(const pa_pool* pool) { return pool ? pool->impl.num_blocks() : -1; }
+
+int32_t pa_pool_num_cached(const pa_pool* pool) { return pool ? pool->impl.num_cached() : -1; }
 
 int32_t pa_block_refcount(const pa_pool* pool, int32_t block) {
   return pool ? pool->impl.refcount(block) : -1;
@@ -307,15 +316,19 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t* child) {
   return ok();
 }
 
-pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slot_mapping_out,
-                        int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow) {
-  if (!pool || !n_cow) return fail(PA_EINVAL, "pa_seq_append: null pointer");
-  if (n_tokens > 0 && !slot_mapping_out) return fail(PA_EINVAL, "pa_seq_append: slot_mapping_out is null");
+namespace {
+
+pa_status seq_append(const char* fn, pa_pool* pool, int64_t seq, const int32_t* tokens, int32_t n_tokens,
+                     int32_t max_hit, int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t cow_cap,
+                     int32_t* n_cow, int32_t* n_hit) {
+  if (!pool || !n_cow || !n_hit) return fail(PA_EINVAL, std::string(fn) + ": null pointer");
+  if (n_tokens > 0 && !slot_mapping_out) return fail(PA_EINVAL, std::string(fn) + ": slot_mapping_out is null");
   if (cow_cap < 1 || !cow_pairs_out)
-    return fail(PA_EINVAL, "pa_seq_append: cow_pairs_out must hold at least one pair");
+    return fail(PA_EINVAL, std::string(fn) + ": cow_pairs_out must hold at least one pair");
   std::string err;
   int32_t src = -1, dst = -1;
-  const pa::PoolResult r = pool->impl.append(seq, n_tokens, slot_mapping_out, &src, &dst, n_cow, &err);
+  const pa::PoolResult r =
+      pool->impl.append(seq, n_tokens, tokens, max_hit, slot_mapping_out, &src, &dst, n_cow, n_hit, &err);
   if (r == pa::PoolResult::kNoMemory) return fail(PA_ENOMEM, err);
   if (r != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
   if (*n_cow) {
@@ -323,6 +336,23 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* s
     cow_pairs_out[1] = dst;
   }
   return ok();
+}
+
+}  // namespace
+
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow) {
+  int32_t n_hit = 0;
+  return seq_append("pa_seq_append", pool, seq, nullptr, n_tokens, 0, slot_mapping_out, cow_pairs_out,
+                    cow_cap, n_cow, &n_hit);
+}
+
+pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq, const int32_t* token_ids, int32_t n_tokens,
+                               int32_t max_hit_tokens, int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                               int32_t cow_cap, int32_t* n_cow, int32_t* n_hit) {
+  if (n_tokens > 0 && !token_ids) return fail(PA_EINVAL, "pa_seq_append_tokens: token_ids is null");
+  return seq_append("pa_seq_append_tokens", pool, seq, token_ids, n_tokens, max_hit_tokens, slot_mapping_out,
+                    cow_pairs_out, cow_cap, n_cow, n_hit);
 }
 
 pa_status pa_seq_free(pa_pool* pool, int64_t seq) {

@@ -33,7 +33,6 @@ constexpr int kBlock = 16;   // tokens per KV block
 // skipped tokens) falls back to one 2-byte store per token.
 template <int D>
 __global__ __launch_bounds__(2 * D) void write_kv_kernel(WriteKvArgs a) {
-  constexpr int kChunks = D / 8;
   __shared__ int64_t slot_s[kBlock];
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * kBlock];   // [dim][token]
 

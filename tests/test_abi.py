@@ -170,3 +170,54 @@ def test_pool_matches_model_bit_for_bit(ops, seed):
             t, n = m.block_table(b)
             assert list(tabs[i, :len(t)]) == t and np.all(tabs[i, len(t):] == -7)
             assert ctx[i] == n
+
+
+@settings(max_examples=80, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.integers(0, 4), st.integers(0, 40), st.integers(0, 7), st.integers(0, 3)),
+                min_size=1, max_size=80),
+       st.integers(0, 2 ** 64 - 1))
+def test_prefix_cached_pool_matches_model_bit_for_bit(ops, seed):
+    N, B = 24, 16
+    p, m = pa.BlockPool(N, B, seed, prefix_caching=True), PoolModel(N, B, seed, prefix_caching=True)
+    prompts = [[7] * 64, list(range(64)), [1, 2] * 32, [3] * 16 + [4] * 48]
+    seqs = []
+    for op, n, pick, which in ops:
+        if op == 0 or not seqs:
+            seqs.append((p.create(), m.seq_create()))
+        elif op == 1:
+            a, b = seqs[pick % len(seqs)]
+            seqs.append((p.fork(a), m.seq_fork(b)))
+        elif op in (2, 3):
+            a, b = seqs[pick % len(seqs)]
+            k = m.ntok[b]
+            toks = [prompts[which][(k + i) % 64] for i in range(n)]
+            try:
+                want = m.seq_append_tokens(b, toks, n - pick) if op == 2 else (*m.seq_append(b, n), 0)
+            except PoolError as e:
+                assert e.code == "ENOMEM"
+                with pytest.raises(pa.PAError) as err:
+                    p.append_tokens(a, toks, n - pick) if op == 2 else p.append(a, n)
+                assert err.value.status == pa.PA_ENOMEM
+            else:
+                got = p.append_tokens(a, toks, n - pick) if op == 2 else (*p.append(a, n), 0)
+                assert tuple(got) == tuple(want)
+        else:
+            a, b = seqs.pop(pick % len(seqs))
+            p.free(a)
+            m.seq_free(b)
+        assert p.num_free == m.num_free() and p.num_cached == m.num_cached()
+        for a, b in seqs:
+            assert p.block_table(a) == m.block_table(b)
+        for blk in range(N):
+            assert p.refcount(blk) == m.refcount(blk)
+
+
+def test_pool_create_ex_rejects_unknown_flags():
+    h = ctypes.c_void_p()
+    assert pa._lib.pa_pool_create_ex(4, 16, 0, 6, ctypes.byref(h)) == pa.PA_EINVAL
+    assert not h.value and "flags" in pa.last_error()
+    assert pa._lib.pa_pool_num_cached(None) == -1
+    p = pa.BlockPool(4, 16, 0)
+    assert p.num_cached == 0
+    s = p.create()
+    assert p.append_tokens(s, list(range(20)), 19)[2] == 0    # caching off: never reuses
