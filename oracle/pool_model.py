@@ -57,6 +57,25 @@ and Cache].  Readings where the pages are silent:
     the head of that list (unmapping its content id);
   * ``append``/``append_tokens`` stay all-or-nothing over the free stack plus
     the evictable list (less the evictable blocks the call itself reuses).
+
+Swapping (optional, ``num_host_blocks > 0``).  The pages fix: under memory
+pressure a sequence's blocks can be moved to CPU memory and brought back
+later, at the cost of host-link bandwidth [IV §Python LLM Inference
+Optimization with vLLM: Parameters That Actually Matter].  Readings:
+  * host swap space is its own pool of host blocks, handed out from a LIFO
+    stack whose initial order is the identity (host block 0 first);
+  * ``swap_out`` moves a whole sequence: for each of its blocks in table
+    order it takes a host block, reports (device, host), and drops the
+    device block's reference (a shared block stays with its other holders;
+    one that reaches zero is released as by ``free``).  All-or-nothing over
+    the host free stack.  The sequence then holds host blocks only and
+    cannot append or fork until swapped in;
+  * ``swap_in`` takes a device block per host block (free stack, then
+    eviction), in table order, reports (host, device), and returns the host
+    blocks to their stack in that order.  All-or-nothing over free plus
+    evictable device blocks.  The new device blocks are not registered for
+    prefix caching (their content ids are not carried over);
+  * ``free`` of a swapped sequence returns its host blocks in table order.
 """
 from __future__ import annotations
 
@@ -71,7 +90,7 @@ class PoolError(Exception):
 
 class PoolModel:
     def __init__(self, num_blocks: int, block_size: int, seed: int = 0,
-                 prefix_caching: bool = False):
+                 prefix_caching: bool = False, num_host_blocks: int = 0):
         if num_blocks <= 0 or block_size <= 0:
             raise PoolError("EINVAL", "num_blocks and block_size must be > 0")
         self.N = num_blocks
@@ -88,10 +107,15 @@ class PoolModel:
         self.content_of_block = [-1] * num_blocks
         self.block_of_content: dict[int, int] = {}
         self.content_ids: dict[tuple, int] = {}   # (previous content id, tokens) -> id
+        self.host_stack = list(range(num_host_blocks - 1, -1, -1))   # top = end: host block 0 first
+        self.host_tables: dict[int, list[int]] = {}   # sequences that are swapped out
 
     # -- queries ---------------------------------------------------------
     def num_free(self) -> int:
         return len(self.stack)
+
+    def num_free_host(self) -> int:
+        return len(self.host_stack)
 
     def num_cached(self) -> int:
         """Registered blocks with no reference, kept for reuse."""
@@ -115,6 +139,7 @@ class PoolModel:
 
     def seq_fork(self, parent: int) -> int:
         self._check(parent)
+        self._resident(parent)
         sid = self.next_id
         self.next_id += 1
         self.tables[sid] = list(self.tables[parent])
@@ -127,6 +152,7 @@ class PoolModel:
     def seq_append(self, seq: int, n_tokens: int):
         """Returns (slot_mapping [n_tokens], cow_pairs [(src, dst)])."""
         self._check(seq)
+        self._resident(seq)
         if n_tokens < 0:
             raise PoolError("EINVAL", "negative token count")
         slots, cow, _ = self._append(seq, [None] * n_tokens, 0)
@@ -136,7 +162,55 @@ class PoolModel:
         """Append tokens with known ids.  Returns (slot_mapping, cow_pairs,
         n_hit): the first n_hit tokens reuse cached blocks (slot -1)."""
         self._check(seq)
+        self._resident(seq)
         return self._append(seq, [int(x) for x in tokens], max(0, int(max_hit_tokens)))
+
+    def seq_swap_out(self, seq: int):
+        """Returns [(device block, host block)] in table order."""
+        self._check(seq)
+        self._resident(seq)
+        table = self.tables[seq]
+        if len(table) > len(self.host_stack):
+            raise PoolError("ENOMEM", f"need {len(table)} host blocks, {len(self.host_stack)} free")
+        pairs, host = [], []
+        for b in table:
+            h = self.host_stack.pop()
+            pairs.append((b, h))
+            host.append(h)
+            self._release(b)
+        self.tables[seq] = []
+        self.host_tables[seq] = host
+        return pairs
+
+    def seq_swap_in(self, seq: int):
+        """Returns [(host block, device block)] in table order."""
+        self._check(seq)
+        if seq not in self.host_tables:
+            raise PoolError("EINVAL", f"sequence {seq} is not swapped out")
+        host = self.host_tables[seq]
+        if len(host) > len(self.stack) + len(self.evictable):
+            raise PoolError("ENOMEM", f"need {len(host)} blocks, "
+                                      f"{len(self.stack) + len(self.evictable)} available")
+        pairs = []
+        for h in host:
+            d = self._take()
+            pairs.append((h, d))
+            self.tables[seq].append(d)
+            self.host_stack.append(h)
+        del self.host_tables[seq]
+        return pairs
+
+    def _release(self, b: int) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            if self.content_of_block[b] >= 0:
+                self.evictable.append(b)
+            else:
+                self.stack.append(b)
+
+    def _resident(self, seq: int) -> None:
+        if seq in self.host_tables:
+            raise PoolError("EINVAL", f"sequence {seq} is swapped out")
 
     def _append(self, seq: int, tokens: list, max_hit: int):
         table = self.tables[seq]
@@ -224,12 +298,9 @@ class PoolModel:
     def seq_free(self, seq: int) -> None:
         self._check(seq)
         for b in self.tables.pop(seq):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                if self.content_of_block[b] >= 0:
-                    self.evictable.append(b)
-                else:
-                    self.stack.append(b)
+            self._release(b)
+        for h in self.host_tables.pop(seq, []):
+            self.host_stack.append(h)
         del self.ntok[seq]
         del self.toks[seq]
 

@@ -265,6 +265,21 @@ class SlotTruth:
     def fork(self, parent, child):
         self.prefix[child] = self.prefix[parent]
 
+    def swap_out(self, pairs):
+        for d, h in pairs:
+            for o in range(self.B):
+                self.slot[("host", h * self.B + o)] = self.slot.get(d * self.B + o)
+
+    def swap_in(self, pairs):
+        for h, d in pairs:
+            for o in range(self.B):
+                self.slot[d * self.B + o] = self.slot.get(("host", h * self.B + o))
+
+    def check_resident(self, m, sid):
+        table, n = m.block_table(sid)
+        for pos in range(n):
+            assert self.slot.get(table[pos // self.B] * self.B + pos % self.B) == self.prefix[sid][:pos + 1]
+
     def apply(self, m, sid, tokens, slots, cow, n_hit):
         for src, dst in cow:
             for o in range(self.B):
@@ -293,6 +308,8 @@ def _check_pool_invariants(m):
         for b in tab:
             live[b] = live.get(b, 0) + 1
     assert m.num_free() + m.num_cached() + len(live) == m.N
+    held = [h for tab in m.host_tables.values() for h in tab]
+    assert len(set(held)) == len(held) and not set(held) & set(m.host_stack)
     for b in range(m.N):
         assert m.ref[b] == live.get(b, 0)
     for b in m.evictable:
@@ -301,12 +318,14 @@ def _check_pool_invariants(m):
 
 
 @settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
-@given(st.lists(st.tuples(st.integers(0, 4), st.integers(0, 40), st.integers(0, 7), st.integers(0, 3)),
+@given(st.lists(st.tuples(st.integers(0, 6), st.integers(0, 40), st.integers(0, 7), st.integers(0, 3)),
                 min_size=1, max_size=60),
        st.integers(0, 2 ** 64 - 1))
-def test_prefix_cache_reuses_only_identical_content(ops, seed):
+def test_prefix_cache_and_swap_keep_every_slot_right(ops, seed):
+    """Reused blocks hold exactly the requester's prefix, and a sequence
+    swapped out and back in finds its whole history in its new blocks."""
     B, N = 4, 40
-    m = PoolModel(N, B, seed, prefix_caching=True)
+    m = PoolModel(N, B, seed, prefix_caching=True, num_host_blocks=24)
     truth = SlotTruth(B)
     seqs = []
     # A few shared "prompts": tokens come from them so that prefixes repeat.
@@ -318,11 +337,35 @@ def test_prefix_cache_reuses_only_identical_content(ops, seed):
             seqs.append(sid)
         elif op == 1:
             parent = seqs[pick % len(seqs)]
+            if parent in m.host_tables:
+                continue
             sid = m.seq_fork(parent)
             truth.fork(parent, sid)
             seqs.append(sid)
+        elif op == 5:
+            sid = seqs[pick % len(seqs)]
+            try:
+                pairs = m.seq_swap_out(sid)
+            except PoolError as e:
+                assert e.code in ("ENOMEM", "EINVAL")
+            else:
+                truth.swap_out(pairs)
+                assert m.block_table(sid)[0] == []
+        elif op == 6:
+            sid = seqs[pick % len(seqs)]
+            try:
+                pairs = m.seq_swap_in(sid)
+            except PoolError as e:
+                assert e.code in ("ENOMEM", "EINVAL")
+            else:
+                truth.swap_in(pairs)
+                truth.check_resident(m, sid)
         elif op in (2, 3):
             sid = seqs[pick % len(seqs)]
+            if sid in m.host_tables:
+                with pytest.raises(PoolError):
+                    m.seq_append(sid, 1)
+                continue
             k = m.ntok[sid]
             src = prompts[which]
             tokens = [src[(k + i) % len(src)] for i in range(n)] if op == 2 else [None] * n
@@ -394,3 +437,38 @@ def test_prefix_cache_off_is_the_plain_pool():
             u = m.seq_create()
             assert m.seq_append_tokens(u, [1] * 9, 8)[2] == 0    # no hits without caching
         assert a.stack == b.stack and a.tables == b.tables and a.num_cached() == 0
+
+
+def test_swap_hand_traced():
+    """Swap-out copies each block to a host block in table order and releases
+    the device blocks; swap-in takes fresh device blocks (stack first) and
+    returns the host blocks in order.  A shared block keeps its other holder."""
+    m = PoolModel(12, 4, 0, num_host_blocks=4)
+    a = m.seq_create()
+    m.seq_append(a, 9)                                  # blocks 0, 1, 2
+    f = m.seq_fork(a)                                   # shares all three
+    assert m.seq_swap_out(a) == [(0, 0), (1, 1), (2, 2)]
+    assert m.refcount(0) == 1 and m.num_free_host() == 1 and m.block_table(a) == ([], 9)
+    with pytest.raises(PoolError):
+        m.seq_append(a, 1)
+    with pytest.raises(PoolError):
+        m.seq_swap_out(a)
+    m.seq_free(f)                                       # now 0, 1, 2 go back (2 on top)
+    c = m.seq_create()
+    m.seq_append(c, 8)                                  # takes 2, then 1
+    assert m.block_table(c)[0] == [2, 1]
+    assert m.seq_swap_in(a) == [(0, 0), (1, 3), (2, 4)]
+    assert m.block_table(a) == ([0, 3, 4], 9) and m.host_stack == [3, 0, 1, 2]
+    with pytest.raises(PoolError) as e:
+        m.seq_swap_in(a)
+    assert e.value.code == "EINVAL"
+    # all-or-nothing on host space
+    big = m.seq_create()
+    m.seq_append(big, 4 * 3)
+    g = m.seq_create()
+    m.seq_append(g, 4 * 2)
+    m.seq_swap_out(big)
+    before = (list(m.stack), list(m.host_stack), dict(m.tables))
+    with pytest.raises(PoolError) as e:
+        m.seq_swap_out(g)                               # needs 2 host blocks, 1 free
+    assert e.value.code == "ENOMEM" and (m.stack, m.host_stack) == before[:2]
