@@ -24,7 +24,8 @@ built through the block pool), mixed (slot-mapped write + 2 prefill chunks +
 two 2048-row chunks alone, without its decode batch: the MFMA-bound part,
 reported against the matrix-core roofline), and prefix_cache (a RAG-shaped
 batch of 32 requests sharing one 1024-token document, written and prefilled
-with and without automatic prefix caching).
+with and without automatic prefix caching), and swap (scattered blocks to
+pinned host memory and back, against the host link's rate).
 """
 from __future__ import annotations
 
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill",
-                             "prefix_cache"])
+                             "prefix_cache", "swap"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's own, 0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -307,6 +308,65 @@ def bench_prefix_cache(args, np, torch, pa):
     return 0
 
 
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args, np, torch, pa):
+    """Swap traffic at the 8B-GQA cache shape (8 KV heads, head_dim 128,
+    bf16, 64 KiB of K + V per block): 4096 scattered device blocks go to
+    scattered blocks of a pinned host swap space and back, each direction one
+    pa_swap_blocks launch.  A contiguous DMA copy of the same byte count
+    (torch's pinned <-> device copy) is timed beside it as the achievable
+    host-link rate."""
+    N, NH, NSW, H, D, B = 6144, 4608, 4096, 8, 128, 16
+    rng = np.random.Generator(np.random.PCG64(4231))
+    dev_ids = rng.permutation(N)[:NSW].astype(np.int32)
+    host_ids = rng.permutation(NH)[:NSW].astype(np.int32)
+    g = torch.Generator(device="cuda").manual_seed(4231)
+    dt = torch.bfloat16
+    kc = torch.randn(N, H, B, D, generator=g, device="cuda").to(dt)
+    vc = torch.randn(N, H, D, B, generator=g, device="cuda").to(dt)
+    hk = torch.empty(NH, H, B, D, dtype=dt).pin_memory()
+    hv = torch.empty(NH, H, D, B, dtype=dt).pin_memory()
+    out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], 1)).cuda()
+    nbytes = NSW * 2 * H * B * D * 2
+    flat_h = torch.empty(nbytes // 2, dtype=dt).pin_memory()
+    flat_d = torch.empty(nbytes // 2, dtype=dt, device="cuda")
+    timer = StepTimer(torch, evict=not args.warm_cache)
+    fns = {
+        "swap_out": lambda: pa.swap_blocks(kc, vc, hk, hv, out_pairs, pa.PA_SWAP_OUT),
+        "swap_in": lambda: pa.swap_blocks(kc, vc, hk, hv, in_pairs, pa.PA_SWAP_IN),
+        "dma_d2h": lambda: flat_h.copy_(flat_d, non_blocking=True),
+        "dma_h2d": lambda: flat_d.copy_(flat_h, non_blocking=True),
+    }
+    res = {}
+    for k, fn in fns.items():
+        timer.run(args.warmup, [fn])
+        per, total, wall = timer.run(args.steps, [fn])
+        ms = mean(total)
+        res[k] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    rt_ms = (res["swap_out"]["us"] + res["swap_in"]["us"]) / 1e3
+    gbs = round(2 * nbytes / (rt_ms * 1e-3) / 1e9, 2)
+    line = {
+        "metric": "KV swap GB/s over the host link (swap-out + swap-in of scattered blocks)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(rt_ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"swap: {NSW} scattered blocks of {N} (8 KV heads, head_dim 128, bf16, 64 KiB "
+                               f"each) to scattered blocks of a {NH}-block pinned host swap space and back; "
+                               "step = one swap-out + one swap-in launch",
+                   "bytes_each_way": nbytes, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "pcie", "achieved": gbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_swap_blocks (copy_blocks_kernel over mapped host memory)"},
+        "directions": res,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -328,6 +388,8 @@ def main():
     name = args.workload
     if name == "prefix_cache":
         return bench_prefix_cache(args, np, torch, pa)
+    if name == "swap":
+        return bench_swap(args, np, torch, pa)
     w = W.mixed(num_decode=0) if name == "prefill" else W.make_workload(name)
     timer = StepTimer(torch, evict=not args.warm_cache)
     extra = {}

@@ -102,6 +102,31 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
                          pa_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Swapping blocks between the device cache and host memory: under memory
+ * pressure a sequence's blocks can move to CPU memory and come back later,
+ * at host-link cost ("Inside vLLM ...", section "Python LLM Inference
+ * Optimization with vLLM: Parameters That Actually Matter").
+ *   host_k, host_v  pinned host memory (hipHostMalloc, e.g. a torch tensor
+ *                   made with pin_memory=True) of num_host_blocks blocks in
+ *                   the caches' layout; the kernel reads or writes it
+ *                   directly over the host link.  Anything else is PA_EINVAL.
+ *   pairs           [num_pairs][2] int32, device: (src, dst) block ids,
+ *                   PA_SWAP_OUT (device -> host): (device, host);
+ *                   PA_SWAP_IN  (host -> device): (host, device).
+ * Copies K and V of every KV head, bit-exact, in one launch; ids out of
+ * range skip the pair.  Pairs run concurrently: a dst must not be the src or
+ * dst of another pair.  Stream-ordered like every device call: enqueue a
+ * swap-out before anything that reuses the released device blocks.
+ * ---------------------------------------------------------------------- */
+#define PA_SWAP_OUT 0
+#define PA_SWAP_IN 1
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
+                         void* host_k, void* host_v, int64_t num_host_blocks,
+                         const int32_t* pairs, int32_t num_pairs, int32_t direction,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Paged decode attention: one query token per sequence attends to all
  * context_lens[s] keys of its sequence (the newest token's K/V must already be
  * written).  Query head h reads KV head h / (num_q_heads / num_kv_heads).
@@ -204,11 +229,14 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed,
  * Without PA_POOL_PREFIX_CACHING the pool behaves exactly as pa_pool_create's
  * (and pa_seq_append_tokens never reuses). */
 #define PA_POOL_PREFIX_CACHING 1u
-/* flags: 0 or PA_POOL_PREFIX_CACHING; other bits give PA_EINVAL. */
+/* flags: 0 or PA_POOL_PREFIX_CACHING; other bits give PA_EINVAL.
+ * num_host_blocks: size of the host swap space (0: no swapping). */
 pa_status pa_pool_create_ex(int32_t num_blocks, int32_t block_size, uint64_t seed,
-                            uint32_t flags, pa_pool** out);
+                            uint32_t flags, int32_t num_host_blocks, pa_pool** out);
 /* Cached blocks (no references, content kept); -1 if pool is NULL. */
 int32_t   pa_pool_num_cached(const pa_pool* pool);
+/* Free host swap blocks; -1 if pool is NULL. */
+int32_t   pa_pool_num_free_host(const pa_pool* pool);
 void      pa_pool_destroy(pa_pool* pool);                 /* NULL-safe */
 int32_t   pa_pool_num_free(const pa_pool* pool);          /* -1 if pool is NULL */
 int32_t   pa_pool_num_blocks(const pa_pool* pool);        /* -1 if pool is NULL */
@@ -245,6 +273,23 @@ pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq, const int32_t* token_
  * reach zero go back on the free stack in that order (registered blocks, with
  * prefix caching, to the tail of the cached list instead). */
 pa_status pa_seq_free(pa_pool* pool, int64_t seq);
+/* Swapping a whole sequence (see pa_swap_blocks).  Host swap blocks come
+ * from a LIFO stack whose initial order is the identity (host block 0 first).
+ * pa_seq_swap_out: for each block in table order takes a host block, writes
+ * (device, host) to pairs_out [cap][2] (host) and drops the device block's
+ * reference (a shared block stays with its other holders; one reaching zero
+ * is released as by pa_seq_free).  The sequence then holds no device blocks
+ * (an empty table, its token count kept) and cannot append or fork until
+ * swapped in.  pa_seq_swap_in: takes a device block per host block (free
+ * stack, then eviction of cached blocks), writes (host, device), returns the
+ * host blocks to their stack in table order; the new blocks are not
+ * registered for prefix caching.  Both are all-or-nothing (PA_ENOMEM) and
+ * need cap >= the sequence's block count (else PA_EINVAL, nothing changed).
+ * pa_seq_free of a swapped-out sequence returns its host blocks. */
+pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq, int32_t* pairs_out, int32_t cap,
+                          int32_t* n_pairs);
+pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq, int32_t* pairs_out, int32_t cap,
+                         int32_t* n_pairs);
 /* Block table of one sequence: up to cap ids into out (host). */
 pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap,
                              int32_t* n_blocks, int32_t* n_tokens);

@@ -38,3 +38,19 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> None:
     for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
         k_cache[dst] = k_cache[src]
         v_cache[dst] = v_cache[src]
+
+
+def swap_blocks(dev_k: np.ndarray, dev_v: np.ndarray, host_k: np.ndarray, host_v: np.ndarray,
+                pairs, direction: int) -> None:
+    """Whole-block copies between the device caches and host swap space of
+    the same layout, in pair order: direction 0 copies device block src to
+    host block dst, direction 1 host block src to device block dst; a pair
+    with an id outside its side's range is skipped.  Moving a sequence's
+    blocks to CPU memory and back ("Inside vLLM ...", section "Python LLM
+    Inference Optimization with vLLM: Parameters That Actually Matter")."""
+    src_k, src_v, dst_k, dst_v = ((dev_k, dev_v, host_k, host_v) if direction == 0
+                                  else (host_k, host_v, dev_k, dev_v))
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        if 0 <= src < src_k.shape[0] and 0 <= dst < dst_k.shape[0]:
+            dst_k[dst] = src_k[src]
+            dst_v[dst] = src_v[src]

@@ -31,6 +31,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_ENOTSUP = range(5)
 PA_POOL_PREFIX_CACHING = 1          # pa_pool_create_ex flag
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1      # pa_swap_blocks directions
 PA_FP16, PA_BF16 = 0, 1
 _STATUS = {1: "EINVAL", 2: "ENOMEM", 3: "EHIP", 4: "ENOTSUP"}
 
@@ -53,8 +54,13 @@ _SIGS = {
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "pa_pool_create": (c_i32, [c_i32, c_i32, c_u64, ctypes.POINTER(c_vp)]),
-    "pa_pool_create_ex": (c_i32, [c_i32, c_i32, c_u64, ctypes.c_uint32, ctypes.POINTER(c_vp)]),
+    "pa_pool_create_ex": (c_i32, [c_i32, c_i32, c_u64, ctypes.c_uint32, c_i32, ctypes.POINTER(c_vp)]),
     "pa_pool_num_cached": (c_i32, [c_vp]),
+    "pa_pool_num_free_host": (c_i32, [c_vp]),
+    "pa_seq_swap_out": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32]),
+    "pa_seq_swap_in": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32]),
+    "pa_swap_blocks": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32, c_i32,
+                               c_i32, c_i32, c_vp]),
     "pa_pool_destroy": (None, [c_vp]),
     "pa_pool_num_free": (c_i32, [c_vp]),
     "pa_pool_num_blocks": (c_i32, [c_vp]),
@@ -135,6 +141,18 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None):
                                H, D, B, _dtype_code(k_cache), _stream(stream)))
 
 
+def swap_blocks(k_cache, v_cache, host_k, host_v, pairs, direction, stream=None):
+    """Whole-block copies between the device caches and pinned host tensors of
+    the same layout (pin_memory=True).  pairs int32 [n, 2] device tensor:
+    (device, host) for PA_SWAP_OUT, (host, device) for PA_SWAP_IN."""
+    N, H, B, D = k_cache.shape
+    if not (host_k.is_pinned() and host_v.is_pinned()):
+        raise PAError(PA_EINVAL, "swap_blocks: host tensors must be pinned")
+    _check(_lib.pa_swap_blocks(_ptr(k_cache), _ptr(v_cache), N, host_k.data_ptr(), host_v.data_ptr(),
+                               host_k.shape[0], _ptr(pairs), pairs.shape[0], direction, H, D, B,
+                               _dtype_code(k_cache), _stream(stream)))
+
+
 def default_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                            max_context_len: int) -> int:
     return int(_lib.pa_default_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -187,10 +205,11 @@ class BlockPool:
     """Refcounted block pool with copy-on-write (host side, ids only)."""
 
     def __init__(self, num_blocks: int, block_size: int = 16, seed: int = 0,
-                 prefix_caching: bool = False):
+                 prefix_caching: bool = False, num_host_blocks: int = 0):
         h = c_vp()
         flags = PA_POOL_PREFIX_CACHING if prefix_caching else 0
-        _check(_lib.pa_pool_create_ex(num_blocks, block_size, seed, flags, ctypes.byref(h)))
+        _check(_lib.pa_pool_create_ex(num_blocks, block_size, seed, flags, num_host_blocks,
+                                      ctypes.byref(h)))
         self._h = h
         self.block_size = block_size
 
@@ -214,6 +233,26 @@ class BlockPool:
     @property
     def num_cached(self) -> int:
         return int(_lib.pa_pool_num_cached(self._h))
+
+    @property
+    def num_free_host(self) -> int:
+        return int(_lib.pa_pool_num_free_host(self._h))
+
+    def _swap(self, fn, seq: int):
+        nb, nt = c_i32(), c_i32()
+        cap = self.num_blocks + 1
+        buf = (c_i32 * (2 * cap))()
+        n = c_i32(0)
+        _check(fn(self._h, seq, buf, cap, ctypes.byref(n)))
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
+
+    def swap_out(self, seq: int):
+        """[(device block, host block)] in table order."""
+        return self._swap(_lib.pa_seq_swap_out, seq)
+
+    def swap_in(self, seq: int):
+        """[(host block, device block)] in table order."""
+        return self._swap(_lib.pa_seq_swap_in, seq)
 
     def refcount(self, block: int) -> int:
         return int(_lib.pa_block_refcount(self._h, block))

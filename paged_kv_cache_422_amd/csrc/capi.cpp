@@ -18,7 +18,8 @@
 
 struct pa_pool {
   pa::BlockPool impl;
-  pa_pool(int32_t n, int32_t b, uint64_t seed, bool caching) : impl(n, b, seed, caching) {}
+  pa_pool(int32_t n, int32_t b, uint64_t seed, bool caching, int32_t host)
+      : impl(n, b, seed, caching, host) {}
 };
 
 namespace {
@@ -122,9 +123,58 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, const
   if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "pa_copy_blocks: null pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ENOTSUP, "pa_copy_blocks: caches must be 16-byte aligned");
-  pa::CopyBlocksArgs a{static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       num_blocks, pairs, num_pairs,
+  pa::CopyBlocksArgs a{static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       num_blocks, num_blocks, pairs, num_pairs,
                        static_cast<int64_t>(num_kv_heads) * block_size * head_dim};
+  return hip_result(fn, pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// Device address of a pinned (hipHostMalloc) host buffer; nullptr if the
+// pointer is not host memory the runtime knows.
+void* pinned_device_pointer(const void* host) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error of the query
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost || !attr.devicePointer) return nullptr;
+  return attr.devicePointer;
+}
+
+}  // namespace
+
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks, void* host_k, void* host_v,
+                         int64_t num_host_blocks, const int32_t* pairs, int32_t num_pairs, int32_t direction,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                         void* stream) {
+  const char* fn = "pa_swap_blocks";
+  if (pa_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype)) return st;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_EINVAL, "pa_swap_blocks: direction must be PA_SWAP_OUT or PA_SWAP_IN");
+  if (num_pairs < 0 || num_blocks < 0 || num_host_blocks < 0)
+    return fail(PA_EINVAL, "pa_swap_blocks: negative size");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !host_k || !host_v || !pairs) return fail(PA_EINVAL, "pa_swap_blocks: null pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(host_k) || !aligned16(host_v))
+    return fail(PA_ENOTSUP, "pa_swap_blocks: buffers must be 16-byte aligned");
+  void* dk = pinned_device_pointer(host_k);
+  void* dv = pinned_device_pointer(host_v);
+  if (!dk || !dv)
+    return fail(PA_EINVAL, "pa_swap_blocks: host buffers must be pinned host memory (hipHostMalloc)");
+  const int64_t elems = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;
+  pa::CopyBlocksArgs a{};
+  if (direction == PA_SWAP_OUT) {
+    a = pa::CopyBlocksArgs{static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                           static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                           num_blocks, num_host_blocks, pairs, num_pairs, elems};
+  } else {
+    a = pa::CopyBlocksArgs{static_cast<const uint16_t*>(dk), static_cast<const uint16_t*>(dv),
+                           static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                           num_host_blocks, num_blocks, pairs, num_pairs, elems};
+  }
   return hip_result(fn, pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -274,21 +324,22 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
 // ---------------------------------------------------------------------------
 
 pa_status pa_pool_create_ex(int32_t num_blocks, int32_t block_size, uint64_t seed, uint32_t flags,
-                            pa_pool** out) {
+                            int32_t num_host_blocks, pa_pool** out) {
   if (!out) return fail(PA_EINVAL, "pa_pool_create: out is null");
   *out = nullptr;
-  if (num_blocks <= 0 || block_size <= 0)
-    return fail(PA_EINVAL, "pa_pool_create: num_blocks and block_size must be positive");
+  if (num_blocks <= 0 || block_size <= 0 || num_host_blocks < 0)
+    return fail(PA_EINVAL, "pa_pool_create: num_blocks and block_size must be positive, num_host_blocks >= 0");
   if (flags & ~static_cast<uint32_t>(PA_POOL_PREFIX_CACHING))
     return fail(PA_EINVAL, "pa_pool_create_ex: unknown flags");
-  pa_pool* p = new (std::nothrow) pa_pool(num_blocks, block_size, seed, (flags & PA_POOL_PREFIX_CACHING) != 0);
+  pa_pool* p = new (std::nothrow)
+      pa_pool(num_blocks, block_size, seed, (flags & PA_POOL_PREFIX_CACHING) != 0, num_host_blocks);
   if (!p) return fail(PA_ENOMEM, "pa_pool_create: host allocation failed");
   *out = p;
   return ok();
 }
 
 pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, uint64_t seed, pa_pool** out) {
-  return pa_pool_create_ex(num_blocks, block_size, seed, 0, out);
+  return pa_pool_create_ex(num_blocks, block_size, seed, 0, 0, out);
 }
 
 void pa_pool_destroy(pa_pool* pool) { delete pool; }
@@ -298,6 +349,8 @@ int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->impl.num_fre
 int32_t pa_pool_num_blocks(const pa_pool* pool) { return pool ? pool->impl.num_blocks() : -1; }
 
 int32_t pa_pool_num_cached(const pa_pool* pool) { return pool ? pool->impl.num_cached() : -1; }
+
+int32_t pa_pool_num_free_host(const pa_pool* pool) { return pool ? pool->impl.num_free_host() : -1; }
 
 int32_t pa_block_refcount(const pa_pool* pool, int32_t block) {
   return pool ? pool->impl.refcount(block) : -1;
@@ -353,6 +406,24 @@ pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq, const int32_t* token_
   if (n_tokens > 0 && !token_ids) return fail(PA_EINVAL, "pa_seq_append_tokens: token_ids is null");
   return seq_append("pa_seq_append_tokens", pool, seq, token_ids, n_tokens, max_hit_tokens, slot_mapping_out,
                     cow_pairs_out, cow_cap, n_cow, n_hit);
+}
+
+pa_status pa_seq_swap_out(pa_pool* pool, int64_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+  if (!pool || !n_pairs || (cap > 0 && !pairs_out)) return fail(PA_EINVAL, "pa_seq_swap_out: null pointer");
+  std::string err;
+  const pa::PoolResult r = pool->impl.swap_out(seq, pairs_out, cap, n_pairs, &err);
+  if (r == pa::PoolResult::kNoMemory) return fail(PA_ENOMEM, err);
+  if (r != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+  return ok();
+}
+
+pa_status pa_seq_swap_in(pa_pool* pool, int64_t seq, int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+  if (!pool || !n_pairs || (cap > 0 && !pairs_out)) return fail(PA_EINVAL, "pa_seq_swap_in: null pointer");
+  std::string err;
+  const pa::PoolResult r = pool->impl.swap_in(seq, pairs_out, cap, n_pairs, &err);
+  if (r == pa::PoolResult::kNoMemory) return fail(PA_ENOMEM, err);
+  if (r != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+  return ok();
 }
 
 pa_status pa_seq_free(pa_pool* pool, int64_t seq) {

@@ -20,11 +20,17 @@ struct WriteKvArgs {
   int32_t head_dim;
 };
 
+// Whole-block copies from one cache-shaped buffer pair to another (the same
+// cache for copy-on-write; the device cache and pinned host swap space for
+// swapping).
 struct CopyBlocksArgs {
-  uint16_t* k_cache;
-  uint16_t* v_cache;
-  int64_t num_blocks;
-  const int32_t* pairs;
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  uint16_t* dst_k;
+  uint16_t* dst_v;
+  int64_t src_blocks;         // ids at or past these are skipped
+  int64_t dst_blocks;
+  const int32_t* pairs;       // [num_pairs][2] (src, dst), device
   int32_t num_pairs;
   int64_t block_elems;        // num_kv_heads * block_size * head_dim
 };

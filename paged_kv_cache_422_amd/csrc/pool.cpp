@@ -26,8 +26,10 @@ struct SplitMix64 {
 
 }  // namespace
 
-BlockPool::BlockPool(int32_t num_blocks, int32_t block_size, uint64_t seed, bool prefix_caching)
+BlockPool::BlockPool(int32_t num_blocks, int32_t block_size, uint64_t seed, bool prefix_caching,
+                     int32_t num_host_blocks)
     : num_blocks_(num_blocks), block_size_(block_size), caching_(prefix_caching), ref_(num_blocks, 0) {
+  for (int32_t h = num_host_blocks - 1; h >= 0; --h) host_free_.push_back(h);   // host block 0 first
   // Initial order: Durstenfeld shuffle of [0, N) (seed 0 keeps identity).
   std::vector<int32_t> order(num_blocks);
   for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
@@ -140,6 +142,10 @@ PoolResult BlockPool::fork(int64_t parent, int64_t* child, std::string* err) {
     *err = "pa_seq_fork: unknown sequence " + std::to_string(parent);
     return PoolResult::kInvalid;
   }
+  if (it->second.swapped) {
+    *err = "pa_seq_fork: sequence " + std::to_string(parent) + " is swapped out";
+    return PoolResult::kInvalid;
+  }
   Seq copy = it->second;
   for (int32_t b : copy.blocks) ++ref_[b];
   const int64_t id = next_id_++;
@@ -163,6 +169,10 @@ PoolResult BlockPool::append(int64_t seq, int32_t n, const int32_t* tokens, int3
     return PoolResult::kInvalid;
   }
   Seq& s = it->second;
+  if (s.swapped) {
+    *err = "pa_seq_append: sequence " + std::to_string(seq) + " is swapped out";
+    return PoolResult::kInvalid;
+  }
   const int64_t B = block_size_;
 
   // Whole leading blocks whose content is cached, along the content chain
@@ -236,15 +246,81 @@ PoolResult BlockPool::release(int64_t seq, std::string* err) {
     *err = "pa_seq_free: unknown sequence " + std::to_string(seq);
     return PoolResult::kInvalid;
   }
-  for (int32_t b : it->second.blocks) {
-    if (--ref_[b] != 0) continue;
-    if (caching_ && content_of_block_[b] >= 0) {
-      ev_push_back(b);          // keeps its content until evicted
-    } else {
-      free_.push_back(b);
-    }
-  }
+  for (int32_t b : it->second.blocks) drop(b);
+  for (int32_t h : it->second.host_blocks) host_free_.push_back(h);
   seqs_.erase(it);
+  return PoolResult::kOk;
+}
+
+void BlockPool::drop(int32_t b) {
+  if (--ref_[b] != 0) return;
+  if (caching_ && content_of_block_[b] >= 0) {
+    ev_push_back(b);          // keeps its content until evicted
+  } else {
+    free_.push_back(b);
+  }
+}
+
+PoolResult BlockPool::swap_out(int64_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs, std::string* err) {
+  *n_pairs = 0;
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end() || it->second.swapped) {
+    *err = "pa_seq_swap_out: sequence " + std::to_string(seq) + (it == seqs_.end() ? " unknown" : " already swapped out");
+    return PoolResult::kInvalid;
+  }
+  Seq& s = it->second;
+  const int64_t n = static_cast<int64_t>(s.blocks.size());
+  if (n > cap) {
+    *err = "pa_seq_swap_out: pairs_out holds " + std::to_string(cap) + " pairs, need " + std::to_string(n);
+    return PoolResult::kInvalid;
+  }
+  if (n > static_cast<int64_t>(host_free_.size())) {
+    *err = "pa_seq_swap_out: swap space exhausted (need " + std::to_string(n) + " host blocks, " +
+           std::to_string(host_free_.size()) + " free)";
+    return PoolResult::kNoMemory;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t h = host_free_.back();
+    host_free_.pop_back();
+    pairs[2 * i] = s.blocks[i];
+    pairs[2 * i + 1] = h;
+    s.host_blocks.push_back(h);
+    drop(s.blocks[i]);
+  }
+  s.blocks.clear();
+  s.swapped = true;
+  *n_pairs = static_cast<int32_t>(n);
+  return PoolResult::kOk;
+}
+
+PoolResult BlockPool::swap_in(int64_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs, std::string* err) {
+  *n_pairs = 0;
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end() || !it->second.swapped) {
+    *err = "pa_seq_swap_in: sequence " + std::to_string(seq) + (it == seqs_.end() ? " unknown" : " is not swapped out");
+    return PoolResult::kInvalid;
+  }
+  Seq& s = it->second;
+  const int64_t n = static_cast<int64_t>(s.host_blocks.size());
+  if (n > cap) {
+    *err = "pa_seq_swap_in: pairs_out holds " + std::to_string(cap) + " pairs, need " + std::to_string(n);
+    return PoolResult::kInvalid;
+  }
+  if (n > static_cast<int64_t>(free_.size()) + ev_size_) {
+    *err = "pa_seq_swap_in: pool exhausted (need " + std::to_string(n) + " blocks, " +
+           std::to_string(static_cast<int64_t>(free_.size()) + ev_size_) + " available)";
+    return PoolResult::kNoMemory;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t d = take();
+    pairs[2 * i] = s.host_blocks[i];
+    pairs[2 * i + 1] = d;
+    s.blocks.push_back(d);
+    host_free_.push_back(s.host_blocks[i]);
+  }
+  s.host_blocks.clear();
+  s.swapped = false;
+  *n_pairs = static_cast<int32_t>(n);
   return PoolResult::kOk;
 }
 

@@ -18,6 +18,11 @@
 // key gets a content id the first time it is registered, for good.  Blocks
 // released to zero references keep their content on an LRU evictable list
 // that allocation drains only when the free stack is empty.
+//
+// Optional swap space: under memory pressure a whole sequence can move to
+// host blocks and come back later at host-link cost (same page, section
+// "Python LLM Inference Optimization with vLLM: Parameters That Actually
+// Matter").  Host blocks come from their own LIFO stack (identity order).
 #pragma once
 
 #include <cstdint>
@@ -31,12 +36,14 @@ enum class PoolResult { kOk, kInvalid, kNoMemory };
 
 class BlockPool {
  public:
-  BlockPool(int32_t num_blocks, int32_t block_size, uint64_t seed, bool prefix_caching = false);
+  BlockPool(int32_t num_blocks, int32_t block_size, uint64_t seed, bool prefix_caching = false,
+            int32_t num_host_blocks = 0);
 
   int32_t num_blocks() const { return num_blocks_; }
   int32_t block_size() const { return block_size_; }
   int32_t num_free() const { return static_cast<int32_t>(free_.size()); }
   int32_t num_cached() const { return ev_size_; }
+  int32_t num_free_host() const { return static_cast<int32_t>(host_free_.size()); }
   bool prefix_caching() const { return caching_; }
   int32_t refcount(int32_t block) const;
 
@@ -51,6 +58,11 @@ class BlockPool {
                     int32_t* cow_src, int32_t* cow_dst, int32_t* n_cow, int32_t* n_hit,
                     std::string* err);
   PoolResult release(int64_t seq, std::string* err);
+  // Moves a resident sequence to host blocks: pairs (device, host) in table
+  // order; the device blocks lose one reference each.  cap bounds the pairs.
+  PoolResult swap_out(int64_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs, std::string* err);
+  // Brings a swapped sequence back: pairs (host, device) in table order.
+  PoolResult swap_in(int64_t seq, int32_t* pairs, int32_t cap, int32_t* n_pairs, std::string* err);
   const std::vector<int32_t>* table(int64_t seq) const;
   int64_t num_tokens(int64_t seq) const;
 
@@ -60,6 +72,8 @@ class BlockPool {
     std::vector<int32_t> blocks;
     int64_t tokens = 0;
     std::vector<int64_t> ids;   // token ids, kept only with prefix caching
+    bool swapped = false;
+    std::vector<int32_t> host_blocks;   // while swapped out
   };
   struct Key {
     int64_t prev;                    // content id of the block before, -1 at the start
@@ -72,6 +86,7 @@ class BlockPool {
   };
 
   int32_t take();                          // free stack first, then evict
+  void drop(int32_t b);                    // one reference less; release at zero
   void ev_push_back(int32_t b);
   void ev_remove(int32_t b);
   void register_block(Seq& s, size_t j);
@@ -80,6 +95,7 @@ class BlockPool {
   int32_t block_size_;
   bool caching_;
   std::vector<int32_t> free_;      // LIFO: back() is the top
+  std::vector<int32_t> host_free_; // host swap blocks, LIFO
   std::vector<int32_t> ref_;
   std::unordered_map<int64_t, Seq> seqs_;
   int64_t next_id_ = 1;

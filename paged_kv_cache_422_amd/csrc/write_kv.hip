@@ -99,19 +99,35 @@ __global__ __launch_bounds__(2 * D) void write_kv_kernel(WriteKvArgs a) {
   }
 }
 
-// One workgroup per (src, dst) pair, 16-byte copies of the K and V tiles of
-// every head.  Out-of-range ids skip the pair.
+// One workgroup per (src, dst) pair: 16-byte copies of the K and V tiles of
+// every head, four of each in flight per thread (the source may sit across
+// the host link).  Out-of-range ids skip the pair.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   const int pair = blockIdx.x;
   const int32_t src = a.pairs[2 * pair];
   const int32_t dst = a.pairs[2 * pair + 1];
-  if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks) return;
+  if (src < 0 || dst < 0 || src >= a.src_blocks || dst >= a.dst_blocks) return;
   const int64_t n16 = a.block_elems / 8;    // 16-byte units per block
-  const u32x4* ks = reinterpret_cast<const u32x4*>(a.k_cache + static_cast<int64_t>(src) * a.block_elems);
-  const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_cache + static_cast<int64_t>(src) * a.block_elems);
-  u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + static_cast<int64_t>(dst) * a.block_elems);
-  u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + static_cast<int64_t>(dst) * a.block_elems);
-  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
+  const u32x4* ks = reinterpret_cast<const u32x4*>(a.src_k + static_cast<int64_t>(src) * a.block_elems);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(a.src_v + static_cast<int64_t>(src) * a.block_elems);
+  u32x4* kd = reinterpret_cast<u32x4*>(a.dst_k + static_cast<int64_t>(dst) * a.block_elems);
+  u32x4* vd = reinterpret_cast<u32x4*>(a.dst_v + static_cast<int64_t>(dst) * a.block_elems);
+  constexpr int kUnroll = 4;
+  int64_t i = threadIdx.x;
+  for (; i + (kUnroll - 1) * 256 < n16; i += kUnroll * 256) {
+    u32x4 k[kUnroll], v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      k[u] = ks[i + u * 256];
+      v[u] = vs[i + u * 256];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      kd[i + u * 256] = k[u];
+      vd[i + u * 256] = v[u];
+    }
+  }
+  for (; i < n16; i += 256) {
     kd[i] = ks[i];
     vd[i] = vs[i];
   }

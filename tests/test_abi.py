@@ -214,10 +214,59 @@ def test_prefix_cached_pool_matches_model_bit_for_bit(ops, seed):
 
 def test_pool_create_ex_rejects_unknown_flags():
     h = ctypes.c_void_p()
-    assert pa._lib.pa_pool_create_ex(4, 16, 0, 6, ctypes.byref(h)) == pa.PA_EINVAL
+    assert pa._lib.pa_pool_create_ex(4, 16, 0, 6, 0, ctypes.byref(h)) == pa.PA_EINVAL
     assert not h.value and "flags" in pa.last_error()
+    assert pa._lib.pa_pool_create_ex(4, 16, 0, 0, -1, ctypes.byref(h)) == pa.PA_EINVAL
     assert pa._lib.pa_pool_num_cached(None) == -1
     p = pa.BlockPool(4, 16, 0)
     assert p.num_cached == 0
     s = p.create()
     assert p.append_tokens(s, list(range(20)), 19)[2] == 0    # caching off: never reuses
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.integers(0, 5), st.integers(0, 40), st.integers(0, 7)),
+                min_size=1, max_size=80),
+       st.integers(0, 2 ** 64 - 1), st.booleans())
+def test_swapping_pool_matches_model_bit_for_bit(ops, seed, caching):
+    N, B, H = 24, 16, 10
+    p = pa.BlockPool(N, B, seed, prefix_caching=caching, num_host_blocks=H)
+    m = PoolModel(N, B, seed, prefix_caching=caching, num_host_blocks=H)
+    seqs = []
+    for op, n, pick in ops:
+        if op == 0 or not seqs:
+            seqs.append((p.create(), m.seq_create()))
+            continue
+        a, b = seqs[pick % len(seqs)]
+        if op == 1:
+            calls = (lambda: p.fork(a), lambda: m.seq_fork(b))
+        elif op == 2:
+            toks = [(m.ntok[b] + i) % 5 for i in range(n)]
+            calls = (lambda: p.append_tokens(a, toks, n), lambda: m.seq_append_tokens(b, toks, n))
+        elif op == 3:
+            calls = (lambda: p.swap_out(a), lambda: m.seq_swap_out(b))
+        elif op == 4:
+            calls = (lambda: p.swap_in(a), lambda: m.seq_swap_in(b))
+        else:
+            seqs.pop(pick % len(seqs))
+            p.free(a)
+            m.seq_free(b)
+            calls = None
+        if calls:
+            try:
+                want = calls[1]()
+            except PoolError as e:
+                with pytest.raises(pa.PAError) as err:
+                    calls[0]()
+                assert err.value.status == {"ENOMEM": pa.PA_ENOMEM, "EINVAL": pa.PA_EINVAL}[e.code]
+            else:
+                got = calls[0]()
+                if op == 1:
+                    seqs.append((got, want))
+                else:
+                    assert (tuple(got) if op == 2 else got) == (tuple(want) if op == 2 else want)
+        assert (p.num_free, p.num_cached, p.num_free_host) == (m.num_free(), m.num_cached(), m.num_free_host())
+        for a, b in seqs:
+            assert p.block_table(a) == m.block_table(b)
+        for blk in range(N):
+            assert p.refcount(blk) == m.refcount(blk)

@@ -104,6 +104,20 @@ def test_write_kv_places_tokens_and_skips_negative_slots():
                 assert np.all(kc[b, :, o, :] == 0xFFFF) and np.all(vc[b, :, :, o] == 0xFFFF)
 
 
+def test_swap_blocks_round_trip_and_skips_bad_ids():
+    rng = np.random.default_rng(4)
+    dk = rng.integers(0, 2 ** 16, (6, 2, 4, 8), dtype=np.uint16)
+    dv = rng.integers(0, 2 ** 16, (6, 2, 8, 4), dtype=np.uint16)
+    hk, hv = np.zeros((3, 2, 4, 8), np.uint16), np.zeros((3, 2, 8, 4), np.uint16)
+    k0, v0 = dk.copy(), dv.copy()
+    KC.swap_blocks(dk, dv, hk, hv, [(4, 0), (1, 2), (5, 3), (-1, 1)], 0)   # last two skipped
+    assert np.array_equal(hk[0], k0[4]) and np.array_equal(hv[2], v0[1]) and not hk[1].any()
+    dk[:] = 0
+    dv[:] = 0
+    KC.swap_blocks(dk, dv, hk, hv, [(0, 3), (2, 0), (7, 1)], 1)
+    assert np.array_equal(dk[3], k0[4]) and np.array_equal(dv[0], v0[1]) and not dk[1].any()
+
+
 def test_copy_blocks_copies_whole_blocks_in_order():
     rng = np.random.default_rng(1)
     kc = rng.integers(0, 65535, (5, 2, 16, 4)).astype(np.uint16)
