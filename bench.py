@@ -63,6 +63,8 @@ def parse():
                     help="seconds of oracle work for the cpu_baseline sample (0: skip)")
     ap.add_argument("--warm-cache", action="store_true",
                     help="do not evict the Infinity Cache between steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured into a HIP graph and replayed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 1 GiB (torch's copy kernel), the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -477,6 +479,24 @@ def main():
     ms = mean(total)
     dec_ms = mean(per[-1])                       # pa_decode is the last call of every step
     gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+
+    if args.graph:
+        # The same calls captured once into a HIP graph; each step replays it.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for fn in fns:
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for fn in fns:
+                fn()
+        timer.run(args.warmup, [graph.replay])
+        _, tot_g, wall_g = timer.run(args.steps, [graph.replay])
+        extra["hip_graph"] = {"us_per_step": round(mean(tot_g) * 1e3, 2), "wall_ms_per_step": round(wall_g, 5),
+                              "eager_us_per_step": round(ms * 1e3, 2), "eager_wall_ms_per_step": round(wall, 5)}
 
     if name == "llama8b_gqa" and P != 0:
         # The workload fixes 512-token split-KV partitions; also time the same
