@@ -25,7 +25,9 @@ two 2048-row chunks alone, without its decode batch: the MFMA-bound part,
 reported against the matrix-core roofline), and prefix_cache (a RAG-shaped
 batch of 32 requests sharing one 1024-token document, written and prefilled
 with and without automatic prefix caching), and swap (scattered blocks to
-pinned host memory and back, against the host link's rate).
+pinned host memory and back, against the host link's rate), and beam (beam
+search at width 4: fork, copy-on-write, write and decode per step, and the
+memory that sharing saves).
 """
 from __future__ import annotations
 
@@ -56,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill",
-                             "prefix_cache", "swap"])
+                             "prefix_cache", "swap", "beam"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's own, 0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -369,6 +371,122 @@ def bench_swap(args, np, torch, pa):
     return 0
 
 
+def bench_beam(args, np, torch, pa):
+    """Beam search at width 4 over 64 requests with 1024-token prompts
+    (8B-GQA shape, bf16): every step each new beam picks a parent (seeded,
+    beam 0 likeliest), a parent taken twice is forked, unchosen beams are
+    freed, and every beam appends one token (copy-on-write of a shared last
+    block).  Device work per step: the block copies, the slot-mapped write of
+    256 tokens and a decode over the 256 beams.  Reports the step time and
+    the blocks the shared layout holds against private copies per beam."""
+    R, WID, PROMPT, Hq, Hkv, D, B = 64, 4, 1024, 32, 8, 128, 16
+    steps_total = args.warmup + args.steps
+    max_len = PROMPT + steps_total + 1
+    N = int(1.2 * R * WID * (-(-max_len // B)))
+    rng = np.random.Generator(np.random.PCG64(4232))
+    parent_p = np.array([0.4, 0.3, 0.2, 0.1])
+    g = torch.Generator(device="cuda").manual_seed(4232)
+    dt = torch.bfloat16
+    kc = torch.randn(N, Hkv, B, D, generator=g, device="cuda").to(dt)
+    vc = torch.randn(N, Hkv, D, B, generator=g, device="cuda").to(dt)
+    pool = pa.BlockPool(N, B, 4232)
+    beams = []
+    for _ in range(R):
+        sid = pool.create()
+        pool.append(sid, PROMPT)          # prompt K/V: the cache's random contents stand in for it
+        beams.append([sid] + [pool.fork(sid) for _ in range(WID - 1)])
+    k_new = torch.randn(R * WID, Hkv, D, generator=g, device="cuda").to(dt)
+    v_new = torch.randn(R * WID, Hkv, D, generator=g, device="cuda").to(dt)
+    q = torch.randn(R * WID, Hq, D, generator=g, device="cuda").to(dt)
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+    stride = -(-max_len // B)
+    ws = torch.empty(max(pa.decode_workspace_size(R * WID, Hq, D, max_len, 0, Hkv), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    # Parent choices drawn up front, so the timed host work is the pool's.
+    choices = np.sort(rng.choice(WID, (steps_total, R, WID), p=parent_p), axis=-1).tolist()
+
+    def host_step(i):
+        """Beam bookkeeping for step i (the selection itself is the
+        harness's part); returns the step's pool outputs and the time spent
+        in pool calls."""
+        to_fork, to_free, fork_at = [], [], set()
+        for r in range(R):
+            taken = set()
+            for j, p in enumerate(choices[i][r]):
+                if p in taken:
+                    to_fork.append(beams[r][p])
+                    fork_at.add((r, j))
+                else:
+                    taken.add(p)
+            to_free += [beams[r][p] for p in range(WID) if p not in taken]
+        t0 = time.perf_counter()
+        children = pool.fork_many(to_fork)
+        pool.free_many(to_free)
+        t_pool = time.perf_counter() - t0
+        children = iter(children)
+        for r in range(R):
+            old = beams[r]
+            beams[r] = [next(children) if (r, j) in fork_at else old[p] for j, p in enumerate(choices[i][r])]
+        seqs = [s for req in beams for s in req]
+        t0 = time.perf_counter()
+        slots, cows = pool.append_many(seqs, [1] * len(seqs))
+        tabs, ctx = pool.block_tables(seqs, stride=stride)
+        t_pool += time.perf_counter() - t0
+        return slots, cows, tabs, ctx, t_pool
+
+    host_us, cow_counts, dev_ms, wall_ms = [], [], [], []
+    t_wall = None
+    for i in range(steps_total):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t_wall = time.perf_counter()
+        slots, cows, tabs, ctx, host = host_step(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if cows:
+            pa.copy_blocks(kc, vc, torch.tensor(cows, dtype=torch.int32, device="cuda"))
+        pa.write_kv(k_new, v_new, kc, vc, torch.from_numpy(slots).cuda())
+        bt = torch.from_numpy(tabs).cuda()
+        ctx_t = torch.from_numpy(ctx).cuda()
+        pa.decode(out, q, kc, vc, bt, ctx_t, max_len, scale, 0, ws)
+        e1.record()
+        if i >= args.warmup:
+            host_us.append(host * 1e6)
+            cow_counts.append(len(cows))
+            dev_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_wall) / args.steps * 1e3
+    dev = [a.elapsed_time(b) for a, b in dev_ms]
+    seqs = [s for req in beams for s in req]
+    used = N - pool.num_free
+    private = sum(-(-pool.block_table(s)[1] // B) for s in seqs)
+    kv_bytes = int(sum(pool.block_table(s)[1] for s in seqs)) * 2 * Hkv * D * 2
+    line = {
+        "metric": "beam-search step (width 4): fork / copy-on-write / write / decode, and memory saved by sharing",
+        "value": round(mean(dev) * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(mean(dev), 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"beam: {R} requests x {WID} beams, {PROMPT}-token prompts, 32 query heads over 8 KV "
+                               "heads, head_dim 128, bf16; step = parent choice, fork/free, one token per beam "
+                               "(copy-on-write), block copies + slot-mapped write + decode of all beams",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (mean(dev) * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kv_bytes / (mean(dev) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole device step (block copies + write + decode), logical KV bytes of the last step"},
+        "host_pool_us_per_step": round(float(np.median(host_us)), 1),
+        "copy_on_write_pairs_per_step": round(mean(cow_counts), 2),
+        "wall_ms_per_step": round(wall, 5),
+        "blocks_in_use": int(used), "blocks_if_private": int(private),
+        "memory_saved_by_sharing": round(1 - used / private, 4),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -392,6 +510,8 @@ def main():
         return bench_prefix_cache(args, np, torch, pa)
     if name == "swap":
         return bench_swap(args, np, torch, pa)
+    if name == "beam":
+        return bench_beam(args, np, torch, pa)
     w = W.mixed(num_decode=0) if name == "prefill" else W.make_workload(name)
     timer = StepTimer(torch, evict=not args.warm_cache)
     extra = {}

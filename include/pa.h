@@ -256,6 +256,24 @@ pa_status pa_seq_fork(pa_pool* pool, int64_t parent, int64_t* child);
 pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens,
                         int64_t* slot_mapping_out, int32_t* cow_pairs_out,
                         int32_t cow_cap, int32_t* n_cow);
+/* pa_seq_fork / pa_seq_free for n sequences in one call, in order
+ * (children_out[n], host).  They stop at the first failure (PA_EINVAL,
+ * unknown or swapped-out sequence) with the earlier ones applied; *n_done
+ * counts those. */
+pa_status pa_seq_fork_many(pa_pool* pool, const int64_t* parents, int32_t n,
+                           int64_t* children_out, int32_t* n_done);
+pa_status pa_seq_free_many(pa_pool* pool, const int64_t* seqs, int32_t n, int32_t* n_done);
+/* pa_seq_append for n sequences in one call, in order: seqs[i] gets
+ * n_tokens[i] tokens.  Slots are written back to back into slot_mapping_out
+ * (sum of n_tokens entries), copy-on-write pairs into cow_pairs_out
+ * [cow_cap][2] in the order they happen (at most one per sequence).  Each
+ * sequence's append is all-or-nothing as in pa_seq_append; the call stops at
+ * the first sequence that fails, leaving the earlier ones applied, and
+ * *n_done counts the sequences applied.  Saves a call per sequence in a
+ * decode or beam-search step. */
+pa_status pa_seq_append_many(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens,
+                             int32_t n, int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                             int32_t cow_cap, int32_t* n_cow, int32_t* n_done);
 /* pa_seq_append with the tokens' ids (token_ids[n_tokens], host).  With
  * prefix caching, when the sequence ends on a block boundary, the longest run
  * of leading whole blocks of the new tokens (at most max_hit_tokens tokens)

@@ -68,6 +68,9 @@ _SIGS = {
     "pa_seq_create": (c_i32, [c_vp, P_i64]),
     "pa_seq_fork": (c_i32, [c_vp, c_i64, P_i64]),
     "pa_seq_append": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, c_i32, P_i32]),
+    "pa_seq_append_many": (c_i32, [c_vp, P_i64, P_i32, c_i32, P_i64, P_i32, c_i32, P_i32, P_i32]),
+    "pa_seq_fork_many": (c_i32, [c_vp, P_i64, c_i32, P_i64, P_i32]),
+    "pa_seq_free_many": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
     "pa_seq_append_tokens": (c_i32, [c_vp, c_i64, P_i32, c_i32, c_i32, P_i64, P_i32, c_i32, P_i32,
                                      P_i32]),
     "pa_seq_free": (c_i32, [c_vp, c_i64]),
@@ -274,6 +277,42 @@ class BlockPool:
         n_cow = c_i32(0)
         _check(_lib.pa_seq_append(self._h, seq, n_tokens, slots, cow, 1, ctypes.byref(n_cow)))
         return list(slots[:n_tokens]), ([(cow[0], cow[1])] if n_cow.value else [])
+
+    def fork_many(self, parents):
+        """Forks each parent in order; returns the children's ids."""
+        import numpy as np
+        ids = np.ascontiguousarray(parents, dtype=np.int64)
+        out = np.empty(max(len(ids), 1), dtype=np.int64)
+        done = c_i32(0)
+        _check(_lib.pa_seq_fork_many(self._h, ids.ctypes.data_as(P_i64), len(ids), out.ctypes.data_as(P_i64),
+                                     ctypes.byref(done)))
+        return out[:len(ids)].tolist()
+
+    def free_many(self, seqs):
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        done = c_i32(0)
+        _check(_lib.pa_seq_free_many(self._h, ids.ctypes.data_as(P_i64), len(ids), ctypes.byref(done)))
+
+    def append_many(self, seqs, n_tokens):
+        """Appends n_tokens[i] tokens to seqs[i], in order, in one call.
+        Returns (slots int64 numpy array, cow pairs list).  On failure raises
+        PAError with .n_done = the sequences already applied."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        cnt = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        n = len(ids)
+        slots = np.empty(max(int(cnt.clip(min=0).sum()), 1), dtype=np.int64)
+        cow = np.empty((max(n, 1), 2), dtype=np.int32)
+        n_cow, n_done = c_i32(0), c_i32(0)
+        st_ = _lib.pa_seq_append_many(self._h, ids.ctypes.data_as(P_i64), cnt.ctypes.data_as(P_i32), n,
+                                      slots.ctypes.data_as(P_i64), cow.ctypes.data_as(P_i32), max(n, 1),
+                                      ctypes.byref(n_cow), ctypes.byref(n_done))
+        if st_ != PA_OK:
+            err = PAError(st_, last_error())
+            err.n_done = n_done.value
+            raise err
+        return slots[:int(cnt.clip(min=0).sum())], [tuple(x) for x in cow[:n_cow.value].tolist()]
 
     def append_tokens(self, seq: int, tokens, max_hit_tokens: int):
         """Returns (slots, cow, n_hit); the first n_hit tokens reuse cached

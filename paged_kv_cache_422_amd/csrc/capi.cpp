@@ -400,6 +400,66 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_tokens, int64_t* s
                     cow_cap, n_cow, &n_hit);
 }
 
+pa_status pa_seq_fork_many(pa_pool* pool, const int64_t* parents, int32_t n, int64_t* children_out,
+                           int32_t* n_done) {
+  if (!pool || !n_done || (n > 0 && (!parents || !children_out)))
+    return fail(PA_EINVAL, "pa_seq_fork_many: null pointer");
+  *n_done = 0;
+  if (n < 0) return fail(PA_EINVAL, "pa_seq_fork_many: negative count");
+  for (int32_t i = 0; i < n; ++i) {
+    std::string err;
+    if (pool->impl.fork(parents[i], &children_out[i], &err) != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+    *n_done = i + 1;
+  }
+  return ok();
+}
+
+pa_status pa_seq_free_many(pa_pool* pool, const int64_t* seqs, int32_t n, int32_t* n_done) {
+  if (!pool || !n_done || (n > 0 && !seqs)) return fail(PA_EINVAL, "pa_seq_free_many: null pointer");
+  *n_done = 0;
+  if (n < 0) return fail(PA_EINVAL, "pa_seq_free_many: negative count");
+  for (int32_t i = 0; i < n; ++i) {
+    std::string err;
+    if (pool->impl.release(seqs[i], &err) != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+    *n_done = i + 1;
+  }
+  return ok();
+}
+
+pa_status pa_seq_append_many(pa_pool* pool, const int64_t* seqs, const int32_t* n_tokens, int32_t n,
+                             int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow,
+                             int32_t* n_done) {
+  if (!pool || !n_cow || !n_done || (n > 0 && (!seqs || !n_tokens)))
+    return fail(PA_EINVAL, "pa_seq_append_many: null pointer");
+  *n_cow = 0;
+  *n_done = 0;
+  if (n < 0) return fail(PA_EINVAL, "pa_seq_append_many: negative count");
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) total += n_tokens[i] > 0 ? n_tokens[i] : 0;
+  if (total > 0 && !slot_mapping_out) return fail(PA_EINVAL, "pa_seq_append_many: slot_mapping_out is null");
+  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out))
+    return fail(PA_EINVAL, "pa_seq_append_many: bad cow_pairs_out / cow_cap");
+  int64_t at = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (*n_cow >= cow_cap)
+      return fail(PA_EINVAL, "pa_seq_append_many: cow_pairs_out full (size it for one pair per sequence)");
+    std::string err;
+    int32_t src = -1, dst = -1, one = 0, hit = 0;
+    const pa::PoolResult r = pool->impl.append(seqs[i], n_tokens[i], nullptr, 0, slot_mapping_out + at, &src,
+                                               &dst, &one, &hit, &err);
+    if (r == pa::PoolResult::kNoMemory) return fail(PA_ENOMEM, err);
+    if (r != pa::PoolResult::kOk) return fail(PA_EINVAL, err);
+    if (one) {
+      cow_pairs_out[2 * *n_cow] = src;
+      cow_pairs_out[2 * *n_cow + 1] = dst;
+      ++*n_cow;
+    }
+    at += n_tokens[i];
+    *n_done = i + 1;
+  }
+  return ok();
+}
+
 pa_status pa_seq_append_tokens(pa_pool* pool, int64_t seq, const int32_t* token_ids, int32_t n_tokens,
                                int32_t max_hit_tokens, int64_t* slot_mapping_out, int32_t* cow_pairs_out,
                                int32_t cow_cap, int32_t* n_cow, int32_t* n_hit) {

@@ -270,3 +270,61 @@ def test_swapping_pool_matches_model_bit_for_bit(ops, seed, caching):
             assert p.block_table(a) == m.block_table(b)
         for blk in range(N):
             assert p.refcount(blk) == m.refcount(blk)
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.integers(0, 7), st.integers(0, 20)), min_size=1, max_size=30),
+       st.integers(0, 2 ** 64 - 1))
+def test_append_many_is_appends_in_order(batch, seed):
+    """One batched call equals the same appends one by one, including where
+    it stops when the pool runs dry."""
+    N, B = 20, 16
+    p, m = pa.BlockPool(N, B, seed), PoolModel(N, B, seed)
+    ids = []
+    for i in range(4):
+        a, b = p.create(), m.seq_create()
+        p.append(a, 9 * i)
+        m.seq_append(b, 9 * i)
+        ids.append((a, b))
+    a0, b0 = ids[0]
+    ids += [(p.fork(a0), m.seq_fork(b0)), (p.fork(ids[2][0]), m.seq_fork(ids[2][1]))]
+    seqs = [ids[i % len(ids)] for i, _ in batch]
+    counts = [n for _, n in batch]
+    want_slots, want_cow, done = [], [], 0
+    for (a, b), n in zip(seqs, counts):
+        try:
+            sl, cow = m.seq_append(b, n)
+        except PoolError:
+            break
+        want_slots += sl
+        want_cow += cow
+        done += 1
+    try:
+        slots, cow = p.append_many([a for a, _ in seqs], counts)
+        assert done == len(seqs)
+    except pa.PAError as e:
+        assert e.status == pa.PA_ENOMEM and e.n_done == done
+    else:
+        assert slots.tolist() == want_slots and cow == want_cow
+    for a, b in ids:
+        assert p.block_table(a) == m.block_table(b)
+
+
+def test_fork_many_and_free_many_equal_single_calls():
+    p, m = pa.BlockPool(30, 16, 3), PoolModel(30, 16, 3)
+    a, b = p.create(), m.seq_create()
+    p.append(a, 40)
+    m.seq_append(b, 40)
+    kids = p.fork_many([a, a, a])
+    mk = [m.seq_fork(b) for _ in range(3)]
+    for x, y in zip(kids, mk):
+        assert p.block_table(x) == m.block_table(y)
+    p.free_many([kids[0], kids[2]])
+    m.seq_free(mk[0])
+    m.seq_free(mk[2])
+    assert p.num_free == m.num_free() and p.refcount(p.block_table(a)[0][0]) == 2
+    with pytest.raises(pa.PAError):
+        p.free_many([kids[1], 999])
+    assert p.num_free == m.num_free() + 0 and p.block_table(a)[0]   # kids[1] freed before the failure
+    m.seq_free(mk[1])
+    assert p.num_free == m.num_free()

@@ -1,0 +1,85 @@
+"""A beam-search trace through the pool: every step each new beam picks a
+parent beam (forking it when another new beam already took it), unchosen
+beams are freed, and every beam appends one token (a shared partial last
+block is copied on write).  The device follows with the block copies and the
+slot-mapped write.  At the end each beam's decode must match the oracle on
+that beam's own token history, gathered with no paging at all."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_422_amd as pa
+from oracle import attention as A
+from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+PARENT_P = np.array([0.4, 0.3, 0.2, 0.1])     # beam 0 is the likeliest parent
+
+
+def beam_parents(rng, width):
+    return sorted(rng.choice(width, width, p=PARENT_P).tolist())
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_beam_trace_decodes_each_beams_history(dtype):
+    print(f"beam trace dtype={dtype}", flush=True)
+    R, WID, PROMPT, STEPS, N, H, Hq, D = 3, 4, 40, 30, 96, 2, 8, 64
+    rng = np.random.default_rng(17)
+    g = torch.Generator(device=DEV).manual_seed(17)
+    total_rows = R * PROMPT + R * WID * STEPS
+    k_rows = torch.randn(total_rows, H, D, generator=g, device=DEV).to(dtype)
+    v_rows = torch.randn(total_rows, H, D, generator=g, device=DEV).to(dtype)
+    kc = torch.full((N, H, 16, D), float("nan"), dtype=dtype, device=DEV)
+    vc = torch.full((N, H, D, 16), float("nan"), dtype=dtype, device=DEV)
+    pool = pa.BlockPool(N, 16, 5)
+    next_row = 0
+
+    def write(sid, rows):
+        slots, cow = pool.append(sid, len(rows))
+        if cow:
+            pa.copy_blocks(kc, vc, torch.tensor(cow, dtype=torch.int32, device=DEV))
+        idx = torch.tensor(rows, device=DEV)
+        pa.write_kv(k_rows[idx], v_rows[idx], kc, vc, torch.tensor(slots, dtype=torch.int64, device=DEV))
+
+    beams = []              # per request: list of (seq id, history rows)
+    for r in range(R):
+        sid = pool.create()
+        hist = list(range(next_row, next_row + PROMPT))
+        next_row += PROMPT
+        write(sid, hist)
+        beams.append([(sid, hist)] + [(pool.fork(sid), list(hist)) for _ in range(WID - 1)])
+    n_cow = 0
+    for _ in range(STEPS):
+        for r in range(R):
+            parents = beam_parents(rng, WID)
+            taken, new = set(), []
+            for p in parents:
+                sid, hist = beams[r][p]
+                if p in taken:
+                    new.append((pool.fork(sid), list(hist)))
+                else:
+                    taken.add(p)
+                    new.append((sid, list(hist)))
+            for p in range(WID):
+                if p not in taken:
+                    pool.free(beams[r][p][0])
+            for j, (sid, hist) in enumerate(new):
+                slots, cow = pool.append(sid, 1)
+                if cow:
+                    n_cow += 1
+                    pa.copy_blocks(kc, vc, torch.tensor(cow, dtype=torch.int32, device=DEV))
+                pa.write_kv(k_rows[next_row:next_row + 1], v_rows[next_row:next_row + 1], kc, vc,
+                            torch.tensor(slots, dtype=torch.int64, device=DEV))
+                hist.append(next_row)
+                next_row += 1
+            beams[r] = new
+    assert n_cow > 0
+    seqs = [b for req in beams for b in req]
+    tabs, ctx = pool.block_tables([s for s, _ in seqs], stride=8)
+    q = torch.randn(len(seqs), Hq, D, generator=g, device=DEV).to(dtype)
+    got = run_decode(q, kc, vc, tabs, ctx, int(ctx.max()), 0.125)
+    kb, vb = bits(k_rows), bits(v_rows)
+    want = A.decode_logical(bits(q), [kb[h] for _, h in seqs], [vb[h] for _, h in seqs], 0.125, dtype_name(q))
+    assert_close(got, want, what="beam decode")
