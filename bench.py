@@ -436,6 +436,16 @@ def bench_beam(args, np, torch, pa):
         t_pool += time.perf_counter() - t0
         return slots, cows, tabs, ctx, t_pool
 
+    # Per-step host outputs go up through two alternating pinned staging sets
+    # (asynchronous copies on the stream); a set is refilled only after the
+    # copies that read it have run.
+    nb = R * WID
+    stage = [{"slots": torch.empty(nb, dtype=torch.int64).pin_memory(),
+              "cows": torch.empty(nb, 2, dtype=torch.int32).pin_memory(),
+              "tabs": torch.empty(nb, stride, dtype=torch.int32).pin_memory(),
+              "ctx": torch.empty(nb, dtype=torch.int32).pin_memory()} for _ in range(2)]
+    dev = [{k: torch.empty_like(v, device="cuda") for k, v in st.items()} for st in stage]
+    done = [None, None]
     host_us, cow_counts, dev_ms, wall_ms = [], [], [], []
     t_wall = None
     for i in range(steps_total):
@@ -443,14 +453,24 @@ def bench_beam(args, np, torch, pa):
             torch.cuda.synchronize()
             t_wall = time.perf_counter()
         slots, cows, tabs, ctx, host = host_step(i)
+        sb, db = stage[i % 2], dev[i % 2]
+        if done[i % 2] is not None:
+            done[i % 2].synchronize()
+        sb["slots"].numpy()[:] = slots
+        sb["tabs"].numpy()[:] = tabs
+        sb["ctx"].numpy()[:] = ctx
+        if cows:
+            sb["cows"].numpy()[:len(cows)] = cows
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
+        for k in sb:
+            db[k].copy_(sb[k], non_blocking=True)
+        done[i % 2] = torch.cuda.Event()
+        done[i % 2].record()
         if cows:
-            pa.copy_blocks(kc, vc, torch.tensor(cows, dtype=torch.int32, device="cuda"))
-        pa.write_kv(k_new, v_new, kc, vc, torch.from_numpy(slots).cuda())
-        bt = torch.from_numpy(tabs).cuda()
-        ctx_t = torch.from_numpy(ctx).cuda()
-        pa.decode(out, q, kc, vc, bt, ctx_t, max_len, scale, 0, ws)
+            pa.copy_blocks(kc, vc, db["cows"][:len(cows)])
+        pa.write_kv(k_new, v_new, kc, vc, db["slots"])
+        pa.decode(out, q, kc, vc, db["tabs"], db["ctx"], max_len, scale, 0, ws)
         e1.record()
         if i >= args.warmup:
             host_us.append(host * 1e6)
