@@ -24,6 +24,14 @@
 // updates an online softmax per row in registers, and accumulates
 // O^T[D x 32 rows] += V^T . P^T (D/32 x 4 MFMAs).
 //
+// Precision of P.V.  fp16 data: weights in fp16, one product each (good to
+// 2^-12).  bf16 data: Q.K^T stays in bf16, but V is converted to fp16 while
+// it is staged (exact up to 65504: bf16's 8 significant bits fit in fp16's
+// 11) and P.V runs in fp16 with one product per weight.  bf16 weights alone
+// (8 significant bits) would break the tolerance when a few keys carry the
+// softmax, so a workgroup that meets a V value beyond fp16's range starts
+// over with bf16 weights split into hi + lo halves (two products).
+//
 // Operand layouts.  In LDS the K rows of each 32-key half are stored with
 // bits 2 and 3 of the key index swapped, so the accumulator element i of
 // lane l (half h = l / 32) holds key 16 * (i / 8) + 8 * h + i % 8: the eight
