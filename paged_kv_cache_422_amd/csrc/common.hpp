@@ -88,6 +88,32 @@ template <> struct SplitP<BF16> { static constexpr bool kSplit = true; };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine a value with the one 32 lanes away (lane l with l ^ 32) in VALU.
+// v_permlane32_swap moves lanes 32..63 of its first operand into lanes
+// 0..31 of its second and back, so given the same value twice its two
+// results are (low half, low half) and (high half, high half): every lane
+// sees both halves, with no LDS round trip (unlike a bpermute).  Both halves
+// get the same result (max and + are commutative, bit for bit).
+__device__ __forceinline__ void halves32(float x, float& lo, float& hi) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // Elements into scalars first: bit-casting a vector element in place reads
+  // element 0 for both.
+  const uint32_t r0 = r[0], r1 = r[1];
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float lo, hi;
+  halves32(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  float lo, hi;
+  halves32(x, lo, hi);
+  return lo + hi;
+}
+
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }

@@ -304,7 +304,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[c2][i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(mx);
     // Lazy rescaling: the running maximum moves only when the tile's exceeds
     // it by more than kLazyLog2, so weights stay below 2^kLazyLog2 (the
     // arithmetic is unchanged and fp32 has the range) and the accumulators
@@ -434,7 +434,7 @@ void prefill_kernel(PrefillArgs a) {
   }
 
   const bool poison = __syncthreads_or(bad_id);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = add_xor32(l_run);
   if (!row_ok) return;
   const float inv_nan = poison ? NAN : 0.f;
   uint16_t* op = a.out + out_row * D;
