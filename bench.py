@@ -138,6 +138,41 @@ class StepTimer:
         return per, total, wall
 
 
+def achievable_copy_gbs(torch, nbytes=2 << 30, reps=10):
+    """Device-to-device copy of 2 GiB (read + write bytes per second): the
+    achievable HBM rate on this machine, beside the 8 TB/s peak."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbs
+
+
+def achievable_gemm_tflops(torch, n=8192, reps=10):
+    """bf16 n x n x n matrix product through torch (hipBLASLt): the achievable
+    matrix-core rate on this machine, beside the 2.5 PFLOP/s peak."""
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    del a, b, c
+    return 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def mean(xs):
     return sum(xs) / max(len(xs), 1)
 
@@ -568,6 +603,9 @@ def main():
             "cpu_baseline": None,
             "wall_ms_per_step": round(wall, 5),
         }
+        gemm = achievable_gemm_tflops(torch)
+        line["achievable"] = {"bf16_gemm_tflops": round(gemm, 1), "frac_of_gemm": round(tflops / gemm, 4),
+                              "reference": "torch bf16 8192^3 matrix product (hipBLASLt), same run"}
         print(json.dumps(line), flush=True)
         return 0
 
@@ -619,6 +657,27 @@ def main():
     ms = mean(total)
     dec_ms = mean(per[-1])                       # pa_decode is the last call of every step
     gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+
+    if name in ("llama7b", "llama8b_gqa"):
+        # The same decode over the same context lengths with every sequence's
+        # blocks consecutive and in order: what the scattered layout costs.
+        nb_s = (ctx_np.astype(np.int64) + 15) // 16
+        starts = np.concatenate([[0], np.cumsum(nb_s)[:-1]])
+        bt_c = np.zeros_like(bt_np)
+        for s_i in range(len(ctx_np)):
+            bt_c[s_i, :nb_s[s_i]] = starts[s_i] + np.arange(nb_s[s_i])
+        assert int(nb_s.sum()) <= kc_t.shape[0]
+        bt_ct = torch.from_numpy(bt_c).cuda()
+        fn_c = [lambda: pa.decode(out, q, kc, vc, bt_ct, ctx, w.max_model_len, w.scale, P, ws)]
+        timer.run(args.warmup, fn_c)
+        _, tot_c, _ = timer.run(args.steps, fn_c)
+        gbs_c = kv_bytes / (mean(tot_c) * 1e-3) / 1e9
+        copy = achievable_copy_gbs(torch)
+        extra["achievable"] = {
+            "copy_GBps": round(copy, 1), "frac_of_copy": round(gbs / copy, 4),
+            "contiguous_blocks_GBps": round(gbs_c, 1), "frac_of_contiguous": round(gbs / gbs_c, 4),
+            "reference": "2 GiB device-to-device copy (read + write bytes); the same decode with each "
+                         "sequence's blocks consecutive in memory, same run"}
 
     if args.graph:
         # The same calls captured once into a HIP graph; each step replays it.
