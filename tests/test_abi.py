@@ -328,3 +328,42 @@ def test_fork_many_and_free_many_equal_single_calls():
     assert p.num_free == m.num_free() + 0 and p.block_table(a)[0]   # kids[1] freed before the failure
     m.seq_free(mk[1])
     assert p.num_free == m.num_free()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), pa.PA_ENOTSUP),
+    (dict(block_size=8), pa.PA_ENOTSUP),
+    (dict(num_q_heads=12, num_kv_heads=8), pa.PA_EINVAL),
+    (dict(bt_stride=0), pa.PA_EINVAL),
+    (dict(num_chunks=-1), pa.PA_EINVAL),
+    (dict(), pa.PA_EINVAL),                          # null pointers with work to do
+    (dict(aligned=False), pa.PA_ENOTSUP),
+    (dict(num_chunks=70000), pa.PA_ENOTSUP),
+])
+def test_prefill_rejects_before_launch(kw, code):
+    a = dict(num_chunks=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, bt_stride=8,
+             aligned=True, fake=True)
+    a.update(kw)
+    if code == pa.PA_EINVAL and not kw:
+        p = [None] * 7
+    else:
+        f = ctypes.c_void_p(0x1000 if a["aligned"] else 0x1004)
+        p = [f] * 7
+    st_ = pa._lib.pa_prefill_chunk(p[0], p[1], p[2], p[3], 100, p[4], a["bt_stride"], p[5], p[6],
+                                   a["num_chunks"], 64, 1024, a["num_q_heads"], a["num_kv_heads"],
+                                   a["head_dim"], a["block_size"], 0.1, pa.PA_BF16, None)
+    assert st_ == code, pa.last_error()
+
+
+def test_prefill_and_swap_zero_work_are_noops():
+    assert pa._lib.pa_prefill_chunk(None, None, None, None, 0, None, 1, None, None, 0, 0, 0, 8, 8, 64, 16,
+                                    0.1, pa.PA_FP16, None) == pa.PA_OK
+    assert pa._lib.pa_swap_blocks(None, None, 0, None, None, 0, None, 0, pa.PA_SWAP_OUT, 8, 128, 16,
+                                  pa.PA_BF16, None) == pa.PA_OK
+
+
+@pytest.mark.parametrize("direction,aligned,code", [(2, True, pa.PA_EINVAL), (pa.PA_SWAP_IN, False, pa.PA_ENOTSUP)])
+def test_swap_blocks_rejects_before_launch(direction, aligned, code):
+    f = ctypes.c_void_p(0x1000 if aligned else 0x1008)
+    st_ = pa._lib.pa_swap_blocks(f, f, 10, f, f, 10, f, 3, direction, 8, 128, 16, pa.PA_BF16, None)
+    assert st_ == code, pa.last_error()
