@@ -63,7 +63,8 @@ struct PrefillLds {
   static constexpr int kVRow = kBlock * 2 + 16;    // bytes per V row (one dim of a block)
   static constexpr int kBytesK = kTileKeys * kRow;
   static constexpr int kBytesVBlock = D * kVRow;
-  static constexpr int kBytes = kBytesK + kTileBlocks * kBytesVBlock;
+  static constexpr int kBytesStage = kBytesK + kTileBlocks * kBytesVBlock;
+  static constexpr int kBytes = kBytesStage + 16;  // + the wide flag
 };
 
 template <class X> struct TypeTag { using type = X; };
@@ -165,7 +166,11 @@ void prefill_kernel(PrefillArgs a) {
   const int lim = min(n_cached + my_row, L - 1);              // last visible key of my row
   const int wave_lim = min(n_cached + min(row0 + 31, n - 1), L - 1);    // last key any row of the wave sees
   const int wave_lim_lo = min(n_cached + row0, L - 1);                  // last key every row of the wave sees
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(c) * a.bt_stride;
+  // The table is read through the constant address space: it is not written
+  // while the kernel runs, and a wave-uniform index then becomes a scalar
+  // load, which keeps off the vector-load counter the K/V waits use.
+  typedef const int32_t __attribute__((address_space(4)))* TableRow;
+  const TableRow bt = (TableRow)(a.block_tables + static_cast<int64_t>(c) * a.bt_stride);
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
   const int64_t head_off = static_cast<int64_t>(g) * tile_elems;
@@ -182,13 +187,12 @@ void prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < UPT; ++r) {
       const int u = r * kPrefillThreads + tid;
       // The block of a unit is the same for the whole wave (UPB is a multiple
-      // of 64), so the table entry is a scalar load, which does not share the
-      // vector-load counter the K/V waits use.
+      // of 64), so its table entry is one scalar load.
       const int lb = t * kTileBlocks + (r * kPrefillThreads + w * 64) / UPB;
       const int wu = u % UPB;
       // Blocks past the sequence end read its last block (always valid); the
       // stash zeroes them.
-      int id = __builtin_amdgcn_readfirstlane(bt[min(lb, nb_seq - 1)]);
+      int id = bt[min(lb, nb_seq - 1)];
       if (id < 0 || id >= a.num_blocks) {
         bad_id |= lb < nb_seq;
         id = 0;
@@ -246,6 +250,12 @@ void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x4*>(lds + Lds::kBytesK + b * Lds::kBytesVBlock + dim * Lds::kVRow + h16 * 16) = v;
     }
   };
+
+  // Set by any wave whose stash met a V value beyond fp16's range, read by
+  // every wave after the barrier that publishes the tile.  Thread 0 clears it
+  // before the first barrier of the pass; it is only ever set afterwards.
+  int* const wide_flag = reinterpret_cast<int*>(lds + Lds::kBytesStage);
+  if (tid == 0) *wide_flag = 0;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[DT];
@@ -386,8 +396,14 @@ void prefill_kernel(PrefillArgs a) {
   // bottom (an odd count gets one more, fully masked tile whose compute
   // returns at once): a break between the two halves would merge a path on
   // which set 1 was never loaded into the loop header and force every wait
-  // there to drain all loads.  With kHalf (bf16 data, V as fp16) the pass
-  // gives up as soon as a tile is wide and returns false.
+  // there to drain all loads; for the same reason the pass gives up only at
+  // the bottom.  With kHalf (bf16 data, V as fp16) a wave whose stash met a
+  // wide value sets the flag before the barrier that publishes the tile, and
+  // the flag is read once per pair, after the second such barrier.  It is
+  // never cleared during the pass and no wave can set it again before every
+  // wave has passed the next barrier, so all waves read the same value and
+  // leave together; tiles computed from an unusable fp16 copy meanwhile are
+  // discarded with the pass.
   auto run = [&](auto half_tag) __attribute__((always_inline)) -> bool {
     constexpr bool kHalf = decltype(half_tag)::value;
     fetch(pk0, pv0, 0);
@@ -399,21 +415,21 @@ void prefill_kernel(PrefillArgs a) {
       __syncthreads();                 // every wave is done with the previous tile
       stash(half_tag, pk0, pv0, t, wide);
       if constexpr (kHalf) {
-        if (__syncthreads_or(wide)) return false;   // tile t is in LDS
-      } else {
-        __syncthreads();
+        if (wide) *wide_flag = 1;
       }
+      __syncthreads();                 // tile t is in LDS
       fetch(pk0, pv0, t + 2);
       compute(half_tag, t);
       __syncthreads();
       stash(half_tag, pk1, pv1, t + 1, wide);
       if constexpr (kHalf) {
-        if (__syncthreads_or(wide)) return false;
-      } else {
-        __syncthreads();
+        if (wide) *wide_flag = 1;
       }
+      __syncthreads();
+      const int gave_up = kHalf ? __builtin_amdgcn_readfirstlane(*wide_flag) : 0;
       fetch(pk1, pv1, t + 3);
       compute(half_tag, t + 1);
+      if (gave_up) return false;
       t += 2;
     } while (t < n_tiles);
     return true;
