@@ -39,8 +39,9 @@
 // consecutive accumulator elements, and the matching V^T operand is eight
 // consecutive keys of one dimension, i.e. 16 contiguous bytes of the
 // dim-major V block.  LDS rows are padded by 16 bytes so that the 16-byte
-// operand reads of a wave hit distinct banks.  Row tiles are dispatched
-// heaviest (longest causal range) first.
+// operand reads of a wave hit distinct banks.  Each XCD takes a contiguous
+// run of row blocks of one chunk and head group (so they share its L2), and
+// within it row blocks are dispatched heaviest (longest causal range) first.
 #include <float.h>
 #include <math.h>
 
@@ -76,6 +77,7 @@ __device__ __forceinline__ int swap_bits23(int r) {
 }
 
 constexpr int kPrefillWaves = 8;
+constexpr int kXcds = 8;              // MI355X: 8 XCDs, 32 CUs and one L2 each
 constexpr float kLazyLog2 = 8.f;      // running-maximum slack, log2 units
 #ifndef PF_PREFETCH
 #define PF_PREFETCH 4
@@ -93,7 +95,24 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int UPT = kTileBlocks * UPB / kPrefillThreads;   // units per thread per tensor per tile
   __shared__ __attribute__((aligned(16))) unsigned char lds[Lds::kBytes];
 
-  const int c = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear index, and each
+  // XCD has its own L2.  Renumber them so that XCD x takes a contiguous run
+  // of the (row block, chunk, head group) order: the row blocks of one chunk
+  // and head group, which read the same keys, then share one L2 instead of
+  // streaming those keys through all eight.  The renumbering is a bijection
+  // for any workgroup count (XCD x owns ceil((n - x) / 8) of them).
+  int bx, by, bz;
+  {
+    const int nx = gridDim.x, ny = gridDim.y;
+    const int n = nx * ny * static_cast<int>(gridDim.z);
+    const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const int q8 = n / kXcds, r8 = n % kXcds, x = lin % kXcds;
+    const int v = x * q8 + min(x, r8) + lin / kXcds;
+    bx = v % nx;
+    by = (v / nx) % ny;
+    bz = v / (nx * ny);
+  }
+  const int c = by;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,13 +124,13 @@ void prefill_kernel(PrefillArgs a) {
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   const int tiles_per_wg = kPrefillWaves / hpw;
   const int nhsub = G / hpw;
-  const int g = blockIdx.z / nhsub;
-  const int hsub = blockIdx.z - g * nhsub;
+  const int g = bz / nhsub;
+  const int hsub = bz - g * nhsub;
   const int hq = g * G + hsub * hpw + (w % hpw);
   const int rt = w / hpw;
   const int wg_rows = 32 * tiles_per_wg;
   const int n_rb = (a.max_q_len + wg_rows - 1) / wg_rows;
-  const int rb = n_rb - 1 - static_cast<int>(blockIdx.x);
+  const int rb = n_rb - 1 - bx;
 
   const int r_start = a.q_start_loc[c];
   const int n = a.q_start_loc[c + 1] - r_start;
