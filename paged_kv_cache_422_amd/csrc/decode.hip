@@ -76,9 +76,13 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* k
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     r.k[ks] = *reinterpret_cast<const u32x4*>(kbase + off + 32 * ks);
+  // V is read once per step: non-temporal loads.  Each V load covers whole
+  // 128-byte lines (16 dims x 16 keys x 2 bytes = 512 contiguous bytes); a K
+  // load covers half of each of 16 key rows' lines, and the other half comes
+  // from the next load, which must still find the line in cache.
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
-    r.v[t] = *reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t);
+    r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t));
 }
 
 // W waves share one partition (W = 4 or 8); each keeps two blocks in flight
