@@ -200,7 +200,7 @@ def cpu_oracle_decode(q, kc, vc, block_tables, context_lens, scale, dtype, budge
     order = list(range(len(context_lens))) if seqs is None else list(seqs)
     per_seq = {}
     qh = bits(q)
-    Hkv, D = kc.shape[1], kc.shape[-1]
+    Hkv, D = vc.shape[1], vc.shape[2]
     t0 = time.perf_counter()
     c0 = time.process_time()
     done = bytes_done = 0
@@ -231,7 +231,7 @@ def build_shared_cache(torch, pa, w, k_tok, v_tok):
     block)."""
     pool = pa.BlockPool(w.num_blocks, 16, 7)
     H, D = w.num_kv_heads, w.head_dim
-    kc = torch.zeros((w.num_blocks, H, 16, D), dtype=k_tok.dtype, device="cuda")
+    kc = torch.zeros(pa.k_cache_shape(w.num_blocks, H, D), dtype=k_tok.dtype, device="cuda")
     vc = torch.zeros((w.num_blocks, H, D, 16), dtype=k_tok.dtype, device="cuda")
     seqs = [None] * w.num_seqs
 
@@ -275,7 +275,7 @@ def bench_prefix_cache(args, np, torch, pa):
     num_blocks = int(1.2 * (R + 1) * (L // B))
     g = torch.Generator(device="cuda").manual_seed(4230)
     dt = torch.bfloat16
-    kc = torch.randn(num_blocks, Hkv, B, D, generator=g, device="cuda").to(dt)
+    kc = torch.randn(pa.k_cache_shape(num_blocks, Hkv, D, B), generator=g, device="cuda").to(dt)
     vc = torch.randn(num_blocks, Hkv, D, B, generator=g, device="cuda").to(dt)
 
     def admit(caching):
@@ -363,9 +363,9 @@ def bench_swap(args, np, torch, pa):
     host_ids = rng.permutation(NH)[:NSW].astype(np.int32)
     g = torch.Generator(device="cuda").manual_seed(4231)
     dt = torch.bfloat16
-    kc = torch.randn(N, H, B, D, generator=g, device="cuda").to(dt)
+    kc = torch.randn(pa.k_cache_shape(N, H, D, B), generator=g, device="cuda").to(dt)
     vc = torch.randn(N, H, D, B, generator=g, device="cuda").to(dt)
-    hk = torch.empty(NH, H, B, D, dtype=dt).pin_memory()
+    hk = torch.empty(pa.k_cache_shape(NH, H, D, B), dtype=dt).pin_memory()
     hv = torch.empty(NH, H, D, B, dtype=dt).pin_memory()
     out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], 1)).cuda()
     in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], 1)).cuda()
@@ -422,7 +422,7 @@ def bench_beam(args, np, torch, pa):
     parent_p = np.array([0.4, 0.3, 0.2, 0.1])
     g = torch.Generator(device="cuda").manual_seed(4232)
     dt = torch.bfloat16
-    kc = torch.randn(N, Hkv, B, D, generator=g, device="cuda").to(dt)
+    kc = torch.randn(pa.k_cache_shape(N, Hkv, D, B), generator=g, device="cuda").to(dt)
     vc = torch.randn(N, Hkv, D, B, generator=g, device="cuda").to(dt)
     pool = pa.BlockPool(N, B, 4232)
     beams = []

@@ -29,13 +29,16 @@
  *   - Pointers to 16-bit data must be 16-byte aligned.
  *
  * KV cache storage (one pair of tensors per layer, caller-allocated):
- *   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]   slot-major
+ *   k_cache  [num_blocks][num_kv_heads][head_dim / 32][block_size][32]
  *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
  * Token t of a sequence lives in block block_table[t / block_size], slot
  * t % block_size; its storage address ("slot") is block * block_size + slot.
- * One (block, kv head) tile is contiguous in both tensors (4 KiB at D = 128).
- * V is stored dim-major so that the attention kernels can feed it straight
- * into the matrix cores, whose operands run along the key index for P.V.
+ * Element d of a key sits in 32-dim chunk d / 32 at position d % 32 of its
+ * slot's 64-byte row.  One (block, kv head) tile is contiguous in both
+ * tensors (4 KiB at D = 128).  The layouts serve the matrix-core operands of
+ * the attention kernels: one load of the K operand for a 32-dim step reads a
+ * whole contiguous 1 KiB chunk (16 keys x 32 dims), and V is stored dim-major
+ * because the P.V operands run along the key index.
  *
  * Device data (block ids, slots, context lengths) is checked inside the
  * kernels: an out-of-range slot or pair is skipped by the write and copy

@@ -13,8 +13,9 @@ when a branch writes into a shared block, that block is copied first; the copy
 is a whole-block duplicate of K and V for every KV head.
 
 Operates in place on raw 16-bit patterns (numpy uint16 or float16), so the
-result is compared bit for bit.  Storage format:
-k_cache [N, Hkv, B, D] (slot-major), v_cache [N, Hkv, D, B] (dim-major).
+result is compared bit for bit.  Storage format (the library's documented
+one): k_cache [N, Hkv, D/32, B, 32] (element d of the key in slot s at
+[.., d // 32, s, d % 32]), v_cache [N, Hkv, D, B] (dim-major).
 """
 from __future__ import annotations
 
@@ -29,7 +30,8 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
         if slot < 0:
             continue
         blk, off = divmod(int(slot), block_size)
-        k_cache[blk, :, off, :] = k[i]
+        H, D = k[i].shape
+        k_cache[blk, :, :, off, :] = k[i].reshape(H, D // 32, 32)
         v_cache[blk, :, :, off] = v[i]
 
 

@@ -7,9 +7,10 @@ import fails loudly (build it with ``python __graft_entry__.py``, which
 calls ``__graft_entry__.build()``).
 
 Function names and arguments follow include/pa.h.  Cache tensors use the
-library's storage format:
-    k_cache [num_blocks, num_kv_heads, 16, head_dim]
+library's storage format (``k_cache_shape`` / ``v_cache_shape``):
+    k_cache [num_blocks, num_kv_heads, head_dim // 32, 16, 32]
     v_cache [num_blocks, num_kv_heads, head_dim, 16]
+Element d of a key sits in 32-dim chunk d // 32 at position d % 32.
 """
 from __future__ import annotations
 
@@ -127,19 +128,39 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 16):
+    """Shape of a K cache tensor: 32-dim chunks of each key, slot-major within a chunk."""
+    return (num_blocks, num_kv_heads, head_dim // 32, block_size, 32)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 16):
+    """Shape of a V cache tensor: dim-major within a block."""
+    return (num_blocks, num_kv_heads, head_dim, block_size)
+
+
+def _cache_dims(k_cache, v_cache):
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a K/V cache pair."""
+    N, H, D, B = v_cache.shape
+    if D % 32 or tuple(k_cache.shape) != k_cache_shape(N, H, D, B):
+        raise PAError(PA_EINVAL, f"k_cache shape {tuple(k_cache.shape)} does not match "
+                                 f"v_cache {tuple(v_cache.shape)}: expected {k_cache_shape(N, H, D, B)}")
+    return N, H, B, D
+
+
 def write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
     """k, v [T, Hkv, D] (token stride may exceed Hkv*D); slot_mapping int64 [T]."""
     T, H, D = k.shape
     assert v.shape == k.shape and v.stride() == k.stride()
     assert k.stride(2) == 1 and k.stride(1) == D
+    N, _, B, _ = _cache_dims(k_cache, v_cache)
     _check(_lib.pa_write_kv(_ptr(k), _ptr(v), k.stride(0), _ptr(k_cache), _ptr(v_cache),
-                            k_cache.shape[0], _ptr(slot_mapping), T, H, D, k_cache.shape[2],
+                            N, _ptr(slot_mapping), T, H, D, B,
                             _dtype_code(k), _stream(stream)))
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None):
     """pairs int32 [n, 2] device tensor of (src, dst)."""
-    N, H, B, D = k_cache.shape
+    N, H, B, D = _cache_dims(k_cache, v_cache)
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), N, _ptr(pairs), pairs.shape[0],
                                H, D, B, _dtype_code(k_cache), _stream(stream)))
 
@@ -148,7 +169,8 @@ def swap_blocks(k_cache, v_cache, host_k, host_v, pairs, direction, stream=None)
     """Whole-block copies between the device caches and pinned host tensors of
     the same layout (pin_memory=True).  pairs int32 [n, 2] device tensor:
     (device, host) for PA_SWAP_OUT, (host, device) for PA_SWAP_IN."""
-    N, H, B, D = k_cache.shape
+    N, H, B, D = _cache_dims(k_cache, v_cache)
+    _cache_dims(host_k, host_v)
     if not (host_k.is_pinned() and host_v.is_pinned()):
         raise PAError(PA_EINVAL, "swap_blocks: host tensors must be pinned")
     _check(_lib.pa_swap_blocks(_ptr(k_cache), _ptr(v_cache), N, host_k.data_ptr(), host_v.data_ptr(),
@@ -176,7 +198,7 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len
     ``workspace``: uint8 device tensor of decode_workspace_size() bytes."""
     import torch
     S, Hq, D = q.shape
-    N, Hkv, B, _ = k_cache.shape
+    N, Hkv, B, _ = _cache_dims(k_cache, v_cache)
     need = decode_workspace_size(S, Hq, D, max_context_len, partition_size, Hkv)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -192,7 +214,7 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, q_start_loc, seq_lens,
                   max_seq_len, scale, stream=None):
     """q/out [T, Hq, D] packed; q_start_loc int32 [n+1]; seq_lens int32 [n]."""
     T, Hq, D = q.shape
-    N, Hkv, B, _ = k_cache.shape
+    N, Hkv, B, _ = _cache_dims(k_cache, v_cache)
     _check(_lib.pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
                                  _ptr(block_tables), block_tables.shape[1], _ptr(q_start_loc),
                                  _ptr(seq_lens), seq_lens.shape[0], max_q_len, max_seq_len, Hq,

@@ -66,7 +66,7 @@ __device__ __forceinline__ int partition_start(int p, int nb, int np) {
 
 template <class T, int D>
 struct BlockRegs {
-  u32x4 k[D / 32];   // K rows: key lane%16, dims 32*ks + 8*(lane/16) .. +7
+  u32x4 k[D / 32];   // K: key lane%16, dims 32*ks + 8*(lane/16) .. +7 (chunk ks)
   u32x2 v[D / 16];   // V: dim 16*t + lane%16, keys 4*(lane/16) .. +3
 };
 
@@ -75,11 +75,12 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* k
                                            const uint16_t* vbase, int64_t off) {
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    r.k[ks] = *reinterpret_cast<const u32x4*>(kbase + off + 32 * ks);
-  // V is read once per step: non-temporal loads.  Each V load covers whole
-  // 128-byte lines (16 dims x 16 keys x 2 bytes = 512 contiguous bytes); a K
-  // load covers half of each of 16 key rows' lines, and the other half comes
-  // from the next load, which must still find the line in cache.
+    r.k[ks] = *reinterpret_cast<const u32x4*>(kbase + off + kBlock * 32 * ks);
+  // V is read once per step: non-temporal loads, each covering whole 128-byte
+  // lines (16 dims x 16 keys x 2 bytes = 512 contiguous bytes).  A K load
+  // reads one whole 1 KiB chunk (16 keys x 32 dims) but stays an ordinary
+  // load: with the hint it was slower (past the end a wave re-reads its last
+  // block, which should then still be cached).
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t));
@@ -162,7 +163,7 @@ void decode_partition_kernel(DecodeArgs a) {
 
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
-  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * D + 8 * quad;
+  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
   const uint16_t* vbase = a.v_cache + g * tile_elems + hl * kBlock + 4 * quad;
 
   float m_run = -INFINITY;   // running max of this lane's head (log2 units)

@@ -40,7 +40,7 @@ struct DecodeArgs {
   float* ws_acc;              // [S][Hq][max_parts][D]
   float* ws_ml;               // [S][Hq][max_parts][2]  (max in log2 units, sum)
   const uint16_t* q;          // [S][Hq][D]
-  const uint16_t* k_cache;    // [N][Hkv][16][D]
+  const uint16_t* k_cache;    // [N][Hkv][D/32][16][32]
   const uint16_t* v_cache;    // [N][Hkv][D][16]
   const int32_t* block_tables;
   const int32_t* context_lens;

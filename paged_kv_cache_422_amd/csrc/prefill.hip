@@ -217,7 +217,7 @@ void prefill_kernel(PrefillArgs a) {
         id = 0;
       }
       const int64_t base = static_cast<int64_t>(id) * blk_elems + head_off;
-      pk[r] = *reinterpret_cast<const u32x4*>(a.k_cache + base + (wu / (D / 8)) * D + (wu % (D / 8)) * 8);
+      pk[r] = *reinterpret_cast<const u32x4*>(a.k_cache + base + static_cast<int64_t>(wu) * 8);
       pv[r] = *reinterpret_cast<const u32x4*>(a.v_cache + base + static_cast<int64_t>(wu) * 8);
     }
   };
@@ -234,10 +234,13 @@ void prefill_kernel(PrefillArgs a) {
       const int u = r * kPrefillThreads + tid;
       const int b = u / UPB;
       const int wu = u % UPB;
-      const int kt = b * kBlock + wu / (D / 8);               // key within the tile
+      // K unit wu is 16 bytes of 32-dim chunk wu / 64: key (wu / 4) % 16,
+      // dims 32 * (wu / 64) + 8 * (wu % 4) .. +7.
+      const int kt = b * kBlock + ((wu >> 2) & (kBlock - 1));   // key within the tile
       const int row = (kt & 32) | swap_bits23(kt & 31);
       const bool live = t * kTileBlocks + b < nb_seq;
-      *reinterpret_cast<u32x4*>(lds + row * Lds::kRow + (wu % (D / 8)) * 16) = live ? pk[r] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(lds + row * Lds::kRow + ((wu >> 6) * 4 + (wu & 3)) * 16) =
+          live ? pk[r] : u32x4{0, 0, 0, 0};
       const int dim = wu >> 1;
       const int h16 = wu & 1;
       u32x4 v = pv[r];

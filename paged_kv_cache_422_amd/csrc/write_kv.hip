@@ -7,9 +7,9 @@
 // (same page, section "Copy-on-Write Makes Beam Search Cheap").  Both kernels
 // move raw 16-bit patterns, so they are dtype-agnostic and bit-exact.
 //
-// Storage: k_cache [N][Hkv][16][D] (slot-major), v_cache [N][Hkv][D][16]
-// (dim-major).  HBM-bound: each token moves 2 * Hkv * D * 2 bytes in and the
-// same out.
+// Storage: k_cache [N][Hkv][D/32][16][32] (32-dim chunks, slot-major within
+// a chunk), v_cache [N][Hkv][D][16] (dim-major).  HBM-bound: each token moves
+// 2 * Hkv * D * 2 bytes in and the same out.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,7 +21,10 @@ constexpr int kBlock = 16;   // tokens per KV block
 
 // One workgroup per (16 consecutive tokens, kv head), 2 * D threads.
 //
-// K: thread (chunk c, token i) moves one 16-byte piece of token i's K row.
+// K: thread (chunk c, token i) moves one 16-byte piece of token i's K row:
+// dims 8c .. 8c+7, which sit in 32-dim chunk c / 4 at slot i, piece c % 4.
+// A wave's 64 threads cover one whole 1 KiB chunk of 16 slots, and a decode
+// token (alone in its block) writes four whole 64-byte pieces.
 // V: a V row of a block is the 16 slots of one dim (32 bytes), so a single
 // token only touches 2 bytes of it.  The group's values pass through LDS,
 // transposed to [dim][token]; thread (dim d, half h) then owns tokens
@@ -72,7 +75,8 @@ __global__ __launch_bounds__(2 * D) void write_kv_kernel(WriteKvArgs a) {
     if (sl >= 0) {
       const int64_t blk = sl / kBlock;
       const int off = static_cast<int>(sl - blk * kBlock);
-      *reinterpret_cast<u32x4*>(a.k_cache + blk * blk_elems + head_tile + off * D + c * 8) = kk;
+      *reinterpret_cast<u32x4*>(a.k_cache + blk * blk_elems + head_tile + (c >> 2) * (kBlock * 32) + off * 32 +
+                                (c & 3) * 8) = kk;
     }
   }
 

@@ -31,7 +31,7 @@ def test_beam_trace_decodes_each_beams_history(dtype):
     total_rows = R * PROMPT + R * WID * STEPS
     k_rows = torch.randn(total_rows, H, D, generator=g, device=DEV).to(dtype)
     v_rows = torch.randn(total_rows, H, D, generator=g, device=DEV).to(dtype)
-    kc = torch.full((N, H, 16, D), float("nan"), dtype=dtype, device=DEV)
+    kc = torch.full(pa.k_cache_shape(N, H, D), float("nan"), dtype=dtype, device=DEV)
     vc = torch.full((N, H, D, 16), float("nan"), dtype=dtype, device=DEV)
     pool = pa.BlockPool(N, 16, 5)
     next_row = 0

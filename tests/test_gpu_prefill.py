@@ -31,11 +31,11 @@ def prefill_case(chunks, Hq, Hkv, D, dtype, seed=0):
     g = torch.Generator(device=DEV).manual_seed(seed)
     T = sum(n for _, n in chunks)
     q = torch.randn(T, Hq, D, generator=g, device=DEV).to(dtype)
-    kc = torch.randn(N, Hkv, 16, D, generator=g, device=DEV).to(dtype)
+    kc = torch.randn(pa.k_cache_shape(N, Hkv, D), generator=g, device=DEV).to(dtype)
     vc = torch.randn(N, Hkv, D, 16, generator=g, device=DEV).to(dtype)
     for c, L in enumerate(lens):
         if L % 16:
-            kc[int(bt[c, nb[c] - 1]), :, L % 16:, :] = float("nan")
+            kc[int(bt[c, nb[c] - 1]), :, :, L % 16:, :] = float("nan")
             vc[int(bt[c, nb[c] - 1]), :, :, L % 16:] = float("nan")
     for b in perm[at:]:
         kc[int(b)] = float("nan")

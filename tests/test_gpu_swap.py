@@ -25,9 +25,9 @@ def test_swap_blocks_bit_exact_both_ways(dtype, H, D):
     print(f"swap dtype={dtype} H={H} D={D}", flush=True)
     g = torch.Generator(device=DEV).manual_seed(12)
     N, NH = 20, 9
-    kc = torch.randn(N, H, 16, D, generator=g, device=DEV).to(dtype)
+    kc = torch.randn(pa.k_cache_shape(N, H, D), generator=g, device=DEV).to(dtype)
     vc = torch.randn(N, H, D, 16, generator=g, device=DEV).to(dtype)
-    hk, hv = _pinned_like(NH, (H, 16, D), dtype), _pinned_like(NH, (H, D, 16), dtype)
+    hk, hv = _pinned_like(NH, pa.k_cache_shape(NH, H, D)[1:], dtype), _pinned_like(NH, (H, D, 16), dtype)
     want_dk, want_dv, want_hk, want_hv = bits(kc), bits(vc), bits(hk), bits(hv)
     out_pairs = np.array([[3, 0], [17, 8], [0, 4], [5, 11], [25, 1]], dtype=np.int32)   # last two skipped
     pa.swap_blocks(kc, vc, hk, hv, torch.from_numpy(out_pairs).to(DEV), pa.PA_SWAP_OUT)
@@ -42,7 +42,7 @@ def test_swap_blocks_bit_exact_both_ways(dtype, H, D):
 
 
 def test_swap_blocks_rejects_unpinned_host_memory():
-    kc = torch.zeros(4, 1, 16, 64, dtype=torch.float16, device=DEV)
+    kc = torch.zeros(pa.k_cache_shape(4, 1, 64), dtype=torch.float16, device=DEV)
     vc = torch.zeros(4, 1, 64, 16, dtype=torch.float16, device=DEV)
     host = np.zeros((4, 1, 16, 64), dtype=np.float16)          # ordinary pageable memory
     pairs = torch.tensor([[0, 0]], dtype=torch.int32, device=DEV)
@@ -56,9 +56,9 @@ def test_sequence_swapped_out_and_in_decodes_identically():
     N, NH, H, Hq, D, dtype = 40, 16, 4, 16, 128, torch.bfloat16
     pool = pa.BlockPool(N, 16, 21, num_host_blocks=NH)
     g = torch.Generator(device=DEV).manual_seed(21)
-    kc = torch.full((N, H, 16, D), float("nan"), dtype=dtype, device=DEV)
+    kc = torch.full(pa.k_cache_shape(N, H, D), float("nan"), dtype=dtype, device=DEV)
     vc = torch.full((N, H, D, 16), float("nan"), dtype=dtype, device=DEV)
-    hk, hv = _pinned_like(NH, (H, 16, D), dtype), _pinned_like(NH, (H, D, 16), dtype)
+    hk, hv = _pinned_like(NH, pa.k_cache_shape(NH, H, D)[1:], dtype), _pinned_like(NH, (H, D, 16), dtype)
 
     def grow(sid, n):
         slots, cow = pool.append(sid, n)

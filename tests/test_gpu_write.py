@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _sentinel_cache(N, H, D, dtype):
-    k = torch.full((N, H, 16, D), 0, dtype=torch.int16, device=DEV)
+    k = torch.full(pa.k_cache_shape(N, H, D), 0, dtype=torch.int16, device=DEV)
     v = torch.full((N, H, D, 16), 0, dtype=torch.int16, device=DEV)
     k.fill_(-21555)   # 0xABCD pattern
     v.fill_(-21555)
@@ -100,7 +100,7 @@ def test_write_kv_strided_source():
 def test_copy_blocks_bit_exact(dtype):
     g = torch.Generator(device=DEV).manual_seed(2)
     N, H, D = 30, 8, 128
-    kc = torch.randn(N, H, 16, D, generator=g, device=DEV).to(dtype)
+    kc = torch.randn(pa.k_cache_shape(N, H, D), generator=g, device=DEV).to(dtype)
     vc = torch.randn(N, H, D, 16, generator=g, device=DEV).to(dtype)
     want_k, want_v = bits(kc), bits(vc)
     pairs = np.array([[1, 20], [3, 21], [29, 0], [7, 22], [2, 40]], dtype=np.int32)  # last: out of range

@@ -30,12 +30,17 @@ def rand_bits(rng, shape, dtype):
     return (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation: still a valid bf16
 
 
+def kshape(N, Hkv, D):
+    """K cache shape in the library's storage format: 32-dim chunks, slot-major within a chunk."""
+    return (N, Hkv, D // 32, B, 32)
+
+
 def paged_layout(rng, lens, Hkv, D, dtype, extra=3):
     """Random scattered cache holding per-sequence logical K/V."""
     nb = [-(-L // B) for L in lens]
     N = sum(nb) + extra
     perm = rng.permutation(N)
-    kc = rand_bits(rng, (N, Hkv, B, D), dtype)
+    kc = rand_bits(rng, kshape(N, Hkv, D), dtype)
     vc = rand_bits(rng, (N, Hkv, D, B), dtype)
     bt = np.zeros((len(lens), max(max(nb), 1)), dtype=np.int32)
     at = 0
@@ -80,7 +85,7 @@ def brute_decode(q, kc, vc, bt, lens, scale, dtype, Hkv):
     for s in range(S):
         for h in range(Hq):
             g = h // G
-            K = [[kf[bt[s][t // B], g, t % B, d] for d in range(D)] for t in range(lens[s])]
+            K = [[kf[bt[s][t // B], g, d // 32, t % B, d % 32] for d in range(D)] for t in range(lens[s])]
             V = [[vf[bt[s][t // B], g, d, t % B] for d in range(D)] for t in range(lens[s])]
             out[s, h] = brute_attend(list(qf[s, h]), K, V, A.scale64(scale))
     return out
@@ -107,9 +112,9 @@ def test_widen_known_patterns():
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("case", [
-    dict(lens=[1, 17, 33, 40], Hq=4, Hkv=4, D=8),
-    dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=16),
-    dict(lens=[0, 3, 31], Hq=2, Hkv=1, D=4),
+    dict(lens=[1, 17, 33, 40], Hq=4, Hkv=4, D=32),
+    dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=64),
+    dict(lens=[0, 3, 31], Hq=2, Hkv=1, D=32),
 ])
 def test_decode_matches_brute_force(dtype, case):
     rng = np.random.default_rng(7)
@@ -141,17 +146,19 @@ def test_tiny_workload_shape_brute_force():
 
 def _dense_from_identity(kc, vc, L, g, dtype):
     nb = -(-L // B)
-    K = A.widen(kc[:nb, g], dtype).reshape(-1, kc.shape[-1])[:L]
-    V = A.widen(np.swapaxes(vc[:nb, g], 1, 2), dtype).reshape(-1, kc.shape[-1])[:L]
+    D = vc.shape[2]
+    # K [nb, D/32, B, 32]: key (block j, slot t), dim 32c + e sits at [j, c, t, e]
+    K = A.widen(np.ascontiguousarray(np.swapaxes(kc[:nb, g], 1, 2)), dtype).reshape(-1, D)[:L]
+    V = A.widen(np.swapaxes(vc[:nb, g], 1, 2), dtype).reshape(-1, D)[:L]
     return K, V
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_decode_identity_table_equals_sdpa(dtype):
     rng = np.random.default_rng(11)
-    Hq, Hkv, D, L = 8, 2, 32, 77
+    Hq, Hkv, D, L = 8, 2, 64, 77
     nb = -(-L // B)
-    kc = rand_bits(rng, (nb, Hkv, B, D), dtype)
+    kc = rand_bits(rng, kshape(nb, Hkv, D), dtype)
     vc = rand_bits(rng, (nb, Hkv, D, B), dtype)
     q = rand_bits(rng, (1, Hq, D), dtype)
     bt = np.arange(nb, dtype=np.int32)[None]
@@ -170,10 +177,10 @@ def test_prefill_identity_table_equals_sdpa_with_causal_mask():
     """Chunk of n rows over n_cached already-cached keys: row j may see keys
     0..n_cached+j.  torch gets the same rule as an explicit boolean mask."""
     rng = np.random.default_rng(12)
-    dtype, Hq, Hkv, D, n_cached, n = "bf16", 4, 2, 16, 21, 30
+    dtype, Hq, Hkv, D, n_cached, n = "bf16", 4, 2, 64, 21, 30
     L = n_cached + n
     nb = -(-L // B)
-    kc = rand_bits(rng, (nb, Hkv, B, D), dtype)
+    kc = rand_bits(rng, kshape(nb, Hkv, D), dtype)
     vc = rand_bits(rng, (nb, Hkv, D, B), dtype)
     q = rand_bits(rng, (n, Hq, D), dtype)
     bt = np.arange(nb, dtype=np.int32)[None]
@@ -208,8 +215,8 @@ def test_two_key_closed_form_fixes_scale_and_sign():
 def test_single_key_returns_that_value_exactly():
     rng = np.random.default_rng(3)
     for dtype in ("fp16", "bf16"):
-        kc, vc, bt = paged_layout(rng, [1], 2, 8, dtype)
-        q = rand_bits(rng, (1, 2, 8), dtype)
+        kc, vc, bt = paged_layout(rng, [1], 2, 32, dtype)
+        q = rand_bits(rng, (1, 2, 32), dtype)
         o = A.decode(q, kc, vc, bt, [1], 0.3, dtype)
         v0 = A.widen(vc[bt[0, 0], :, :, 0], dtype)
         assert np.array_equal(o[0], v0)
@@ -237,8 +244,8 @@ def test_dominant_logit_selects_its_value():
 
 def test_empty_context_is_zero_row():
     rng = np.random.default_rng(6)
-    kc, vc, bt = paged_layout(rng, [0, 3], 1, 4, "fp16")
-    q = rand_bits(rng, (2, 1, 4), "fp16")
+    kc, vc, bt = paged_layout(rng, [0, 3], 1, 32, "fp16")
+    q = rand_bits(rng, (2, 1, 32), "fp16")
     o = A.decode(q, kc, vc, bt, [0, 3], 0.5, "fp16")
     assert np.all(o[0] == 0.0) and np.all(np.isfinite(o))
 
@@ -247,7 +254,7 @@ def test_gqa_head_mapping_contiguous_groups():
     """KV head g holds V == g + 1 everywhere, so query head h must return
     h // (Hq / Hkv) + 1 in every coordinate."""
     rng = np.random.default_rng(8)
-    Hq, Hkv, D, L = 8, 2, 4, 20
+    Hq, Hkv, D, L = 8, 2, 32, 20
     kc, vc, bt = paged_layout(rng, [L], Hkv, D, "fp16")
     for g in range(Hkv):
         vc[:, g] = np.float16(g + 1)
@@ -276,8 +283,8 @@ def test_block_permutation_invariance():
     Figured Out Decades Ago'): relabelling physical blocks changes nothing."""
     rng = np.random.default_rng(10)
     lens = [40, 1, 64, 17]
-    kc, vc, bt = paged_layout(rng, lens, 2, 8, "bf16", extra=5)
-    q = rand_bits(rng, (4, 4, 8), "bf16")
+    kc, vc, bt = paged_layout(rng, lens, 2, 32, "bf16", extra=5)
+    q = rand_bits(rng, (4, 4, 32), "bf16")
     base = A.decode(q, kc, vc, bt, lens, 0.35, "bf16")
     pi = rng.permutation(kc.shape[0])
     kc2 = np.empty_like(kc); vc2 = np.empty_like(vc)
@@ -292,7 +299,7 @@ def test_shared_prefix_reads_like_private_copies():
     Search Cheap'): sequences pointing at the same prefix blocks give exactly
     the result of sequences owning private copies."""
     rng = np.random.default_rng(13)
-    Hkv, D, P = 2, 8, 37                      # prefix ends inside block 2
+    Hkv, D, P = 2, 32, 37                     # prefix ends inside block 2
     lens = [P + 5, P + 20, P]
     prefix_k = rand_bits(rng, (P, Hkv, D), "fp16")
     prefix_v = rand_bits(rng, (P, Hkv, D), "fp16")
@@ -306,7 +313,7 @@ def test_shared_prefix_reads_like_private_copies():
     # shared layout: full prefix blocks shared, partial last prefix block
     # copied for every sequence that writes past the prefix.
     N = 40
-    kc = np.zeros((N, Hkv, B, D), np.float16); vc = np.zeros((N, Hkv, D, B), np.float16)
+    kc = np.zeros(kshape(N, Hkv, D), np.float16); vc = np.zeros((N, Hkv, D, B), np.float16)
     shared = [0, 1]                           # holds tokens 0..31
     nxt = 2
     bt = np.zeros((3, 8), np.int32)
@@ -327,7 +334,7 @@ def test_shared_prefix_reads_like_private_copies():
 
 def test_decode_is_last_row_of_prefill_and_chunking_is_invisible():
     rng = np.random.default_rng(14)
-    dtype, Hq, Hkv, D, L = "bf16", 4, 2, 8, 45
+    dtype, Hq, Hkv, D, L = "bf16", 4, 2, 32, 45
     kc, vc, bt = paged_layout(rng, [L], Hkv, D, dtype)
     q = rand_bits(rng, (L, Hq, D), dtype)
     one = A.prefill(q, kc, vc, bt, [0, L], [L], 0.3, dtype)
@@ -382,7 +389,16 @@ def _values_not_transposed(k_cache, v_cache, bt_row, n_tokens, kv_head, block_si
     nb = -(-n_tokens // block_size)
     phys = np.asarray(bt_row[:nb], dtype=np.int64)
     raw = np.ascontiguousarray(v_cache[phys, kv_head])  # read [D, B] as if [B, D]
-    V = A.widen(raw, dtype).reshape(-1, k_cache.shape[-1])[:n_tokens]
+    V = A.widen(raw, dtype).reshape(-1, v_cache.shape[2])[:n_tokens]
+    return K, V
+
+
+def _keys_read_slot_major(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype):
+    _, V = _good_gather(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype)
+    nb = -(-n_tokens // block_size)
+    phys = np.asarray(bt_row[:nb], dtype=np.int64)
+    raw = np.ascontiguousarray(k_cache[phys, kv_head])  # read [D/32, B, 32] as if [B, D]
+    K = A.widen(raw, dtype).reshape(-1, v_cache.shape[2])[:n_tokens]
     return K, V
 
 
@@ -405,12 +421,15 @@ def _wrong_slot(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype):
     ("dropped scale (closed form)", "attend", _no_scale, test_two_key_closed_form_fixes_scale_and_sign),
     ("flipped sign", "attend", _flipped_sign, lambda: test_decode_identity_table_equals_sdpa("fp16")),
     ("off-by-one context", "attend", _drops_last_key, lambda: test_decode_matches_brute_force(
-        "bf16", dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=16))),
+        "bf16", dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=64))),
     ("off-by-one causal (prefill)", "attend", _drops_last_key, test_prefill_identity_table_equals_sdpa_with_causal_mask),
     ("V storage read untransposed", "gather_kv", _values_not_transposed, test_shared_prefix_reads_like_private_copies),
+    ("K chunks read as slot-major rows", "gather_kv", _keys_read_slot_major, lambda: test_decode_identity_table_equals_sdpa("fp16")),
+    ("K chunks read as slot-major rows (brute force)", "gather_kv", _keys_read_slot_major, lambda: test_decode_matches_brute_force(
+        "bf16", dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=64))),
     ("wrong KV head", "gather_kv", _wrong_kv_head, test_gqa_head_mapping_contiguous_groups),
     ("block table order", "gather_kv", _wrong_slot, lambda: test_decode_matches_brute_force(
-        "fp16", dict(lens=[1, 17, 33, 40], Hq=4, Hkv=4, D=8))),
+        "fp16", dict(lens=[1, 17, 33, 40], Hq=4, Hkv=4, D=32))),
 ])
 def test_planted_mistake_trips_a_pin(monkeypatch, name, target, bad, pin):
     monkeypatch.setattr(A, target, bad)

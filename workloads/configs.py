@@ -78,11 +78,12 @@ class DecodeWorkload:
             self.num_kv_heads * self.head_dim * 2
 
     def cache_shapes(self):
+        """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, D, B] (dim-major)."""
         N, H, B, D = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
-        return (N, H, B, D), (N, H, D, B)
+        return (N, H, D // 32, B, 32), (N, H, D, B)
 
     def make_tensors(self, device="cpu", seed_offset=0):
-        """q [S, Hq, D], k_cache [N, Hkv, B, D], v_cache [N, Hkv, D, B]."""
+        """q [S, Hq, D], k_cache [N, Hkv, D/32, B, 32], v_cache [N, Hkv, D, B]."""
         import torch
         g = torch.Generator(device=device)
         g.manual_seed(self.seed + seed_offset)
@@ -265,8 +266,9 @@ class MixedWorkload:
         return self.num_new_tokens * 2 * self.num_kv_heads * self.head_dim * 2 * 2
 
     def cache_shapes(self):
+        """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, D, B] (dim-major)."""
         N, H, B, D = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
-        return (N, H, B, D), (N, H, D, B)
+        return (N, H, D // 32, B, 32), (N, H, D, B)
 
     def make_tensors(self, device="cpu"):
         """Pre-step caches, new k/v [T, Hkv, D], decode q [S_dec, Hq, D],
