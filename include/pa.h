@@ -135,6 +135,8 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
  * written).  Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *
  *   out, q          [num_seqs][num_q_heads][head_dim], contiguous.
+ *   num_blocks      blocks in each cache; must be >= 1 when num_seqs > 0
+ *                   (PA_EINVAL otherwise).
  *   block_tables    [num_seqs][bt_stride] int32, device.
  *   context_lens    [num_seqs] int32, device; 0 gives a zero row; a length
  *                   above max_context_len or bt_stride*block_size gives NaN.
@@ -178,6 +180,8 @@ pa_status pa_decode(void* out, const void* q,
  *
  *   out, q        [total_rows][num_q_heads][head_dim] packed; chunk c owns
  *                 rows q_start_loc[c] .. q_start_loc[c+1]-1.
+ *   num_blocks    blocks in each cache; must be >= 1 when there is a chunk
+ *                 with rows (PA_EINVAL otherwise).
  *   q_start_loc   [num_chunks+1] int32, device, non-decreasing, from 0.
  *   seq_lens      [num_chunks] int32, device: keys of chunk c's sequence
  *                 after the chunk, >= n_c.

@@ -234,6 +234,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
       (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > kMaxPartitionTokens))
     return fail(PA_ENOTSUP, "pa_decode: partition_size must be 0 or a multiple of 16 in [16, 4096]");
   if (num_seqs == 0) return ok();
+  // A bad block id, and a prefetch past a sequence's last block, read block 0.
+  if (num_blocks == 0) return fail(PA_EINVAL, "pa_decode: num_blocks must be positive when num_seqs > 0");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_EINVAL, "pa_decode: null pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -294,6 +296,9 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(PA_EINVAL, "pa_prefill_chunk: num_q_heads must be a positive multiple of num_kv_heads");
   if (num_chunks == 0 || max_q_len == 0) return ok();
+  // A bad block id reads block 0 (its tile is then discarded).
+  if (num_blocks == 0)
+    return fail(PA_EINVAL, "pa_prefill_chunk: num_blocks must be positive when there are chunks");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !q_start_loc || !seq_lens)
     return fail(PA_EINVAL, "pa_prefill_chunk: null pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))

@@ -73,14 +73,12 @@ struct BlockRegs {
 template <class T, int D>
 __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t off) {
+  // K and V are read once per step: non-temporal loads.  Each covers whole
+  // 128-byte lines: a K load one 1 KiB chunk (16 keys x 32 dims), a V load
+  // 16 dims x 16 keys x 2 bytes = 512 contiguous bytes.
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    r.k[ks] = *reinterpret_cast<const u32x4*>(kbase + off + kBlock * 32 * ks);
-  // V is read once per step: non-temporal loads, each covering whole 128-byte
-  // lines (16 dims x 16 keys x 2 bytes = 512 contiguous bytes).  A K load
-  // reads one whole 1 KiB chunk (16 keys x 32 dims) but stays an ordinary
-  // load: with the hint it was slower (past the end a wave re-reads its last
-  // block, which should then still be cached).
+    r.k[ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + kBlock * 32 * ks));
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t));
@@ -239,9 +237,13 @@ void decode_partition_kernel(DecodeArgs a) {
   };
 
   // Software pipeline over three register buffers: the loads of the next two
-  // blocks a wave handles are in flight while it works on the current one.  Prefetches are issued unconditionally (past the end they
-  // re-read the wave's last block, which the cache still holds) so that the
-  // wait before each block only covers that block's own loads.
+  // blocks a wave handles are in flight while it works on the current one.
+  // Prefetches are issued unconditionally, so that the wait before each block
+  // only covers that block's own loads.  Past the end they read block 0 of
+  // the pool (the host rejects an empty pool when there is work): every
+  // wave's out-of-range prefetches share those lines, which then stay in L2,
+  // where re-reading a wave's own last block would go back to HBM under the
+  // non-temporal hint.
   auto blk_off = [&](int jj) {
     const int r = jj >> 6;                    // wave-uniform
     int id = __builtin_amdgcn_readlane(my_bt[0], jj & 63);
@@ -251,22 +253,21 @@ void decode_partition_kernel(DecodeArgs a) {
     return static_cast<int64_t>(id) * blk_elems;
   };
   int j = w;
-  const int j_last = w + ((nblk - 1 - w) / W) * W;   // this wave's last block
-  auto nxt = [&](int jj) { return jj < nblk ? jj : j_last; };
+  auto pf_off = [&](int jj) -> int64_t { return jj < nblk ? blk_off(jj) : int64_t(0); };
   if (j < nblk) {
     BlockRegs<T, D> b0, b1, b2;
     load_block<T, D>(b0, kbase, vbase, blk_off(j));
-    load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + W)));
+    load_block<T, D>(b1, kbase, vbase, pf_off(j + W));
     for (;;) {
-      load_block<T, D>(b2, kbase, vbase, blk_off(nxt(j + 2 * W)));
+      load_block<T, D>(b2, kbase, vbase, pf_off(j + 2 * W));
       process(b0, j);
       j += W;
       if (j >= nblk) break;
-      load_block<T, D>(b0, kbase, vbase, blk_off(nxt(j + 2 * W)));
+      load_block<T, D>(b0, kbase, vbase, pf_off(j + 2 * W));
       process(b1, j);
       j += W;
       if (j >= nblk) break;
-      load_block<T, D>(b1, kbase, vbase, blk_off(nxt(j + 2 * W)));
+      load_block<T, D>(b1, kbase, vbase, pf_off(j + 2 * W));
       process(b2, j);
       j += W;
       if (j >= nblk) break;

@@ -355,6 +355,21 @@ def test_prefill_rejects_before_launch(kw, code):
     assert st_ == code, pa.last_error()
 
 
+def test_decode_and_prefill_reject_an_empty_pool_with_work():
+    """Both kernels read block 0 for a bad block id (and decode for a prefetch
+    past a sequence's end), so a call with work needs at least one block."""
+    f = ctypes.c_void_p(0x1000)
+    st_ = pa._lib.pa_decode(f, f, f, f, 0, f, 16, f, 4, 32, 8, 128, 16, 256, 0.1, 0, f, 1 << 20,
+                            pa.PA_BF16, None)
+    assert st_ == pa.PA_EINVAL and "num_blocks" in pa.last_error()
+    st_ = pa._lib.pa_prefill_chunk(f, f, f, f, 0, f, 8, f, f, 2, 64, 1024, 32, 8, 128, 16, 0.1,
+                                   pa.PA_BF16, None)
+    assert st_ == pa.PA_EINVAL and "num_blocks" in pa.last_error()
+    # no sequences: nothing to read, still fine
+    assert pa._lib.pa_decode(None, None, None, None, 0, None, 16, None, 0, 32, 8, 128, 16, 256, 0.1, 0,
+                             None, 0, pa.PA_BF16, None) == pa.PA_OK
+
+
 def test_prefill_and_swap_zero_work_are_noops():
     assert pa._lib.pa_prefill_chunk(None, None, None, None, 0, None, 1, None, None, 0, 0, 0, 8, 8, 64, 16,
                                     0.1, pa.PA_FP16, None) == pa.PA_OK
