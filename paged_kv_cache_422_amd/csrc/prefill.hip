@@ -366,6 +366,14 @@ void prefill_kernel(PrefillArgs a) {
       using P = typename decltype(ptag)::type;
       constexpr int kPart = decltype(part)::value;
       float psum = 0.f;
+      const unsigned char* vr = vbase + r32 * Lds::kVRow + 16 * half;
+      auto vop = [&](int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4*>(vr + (j / DT) * Lds::kBytesVBlock + 32 * (j % DT) * Lds::kVRow);
+      };
+      u32x4 vb[kPrefetch];
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) vb[j] = vop(j);
+      __builtin_amdgcn_sched_barrier(0);
       u32x4 pB[4];                     // P^T operands of the four 16-key k-steps
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
@@ -385,14 +393,8 @@ void prefill_kernel(PrefillArgs a) {
 
       // O^T += V^T . P^T; k-step kk covers block kk of the tile, keys
       // 8*half .. +7.  Product j = (kk, dt) = (j / DT, j % DT); operands are
-      // read kPrefetch products ahead, as for S^T.
-      const unsigned char* vr = vbase + r32 * Lds::kVRow + 16 * half;
-      auto vop = [&](int j) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4*>(vr + (j / DT) * Lds::kBytesVBlock + 32 * (j % DT) * Lds::kVRow);
-      };
-      u32x4 vb[kPrefetch];
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) vb[j] = vop(j);
+      // read kPrefetch products ahead, as for S^T, the first ones before the
+      // exponentials above (they do not depend on P).
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4 * DT; ++j) {
