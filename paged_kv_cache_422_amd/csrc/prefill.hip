@@ -287,6 +287,19 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
 
   // One key tile: S^T, online softmax, P.V, all from LDS.
+  // The first kPrefetch K operands of a tile, read right after the barrier
+  // that publishes it, ahead of the fetch: the fetch's wait for its table
+  // entries then covers their LDS latency too.
+  const unsigned char* const kr = lds + r32 * Lds::kRow + 16 * half;
+  auto kop = [&](int j) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(kr + (j & 1) * 32 * Lds::kRow + 32 * (j >> 1));
+  };
+  u32x4 kb[kPrefetch];
+  auto preload_k = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) kb[j] = kop(j);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto compute = [&](auto half_tag, int t) __attribute__((always_inline)) {
     const int k0 = t * kTileKeys;
     if (!wave_on || k0 > wave_lim) return;
@@ -301,13 +314,6 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[c2][i] = 0.f;
     {
-      const unsigned char* kr = lds + r32 * Lds::kRow + 16 * half;
-      auto kop = [&](int j) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4*>(kr + (j & 1) * 32 * Lds::kRow + 32 * (j >> 1));
-      };
-      u32x4 kb[kPrefetch];
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) kb[j] = kop(j);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 2 * KS; ++j) {
@@ -442,6 +448,7 @@ void prefill_kernel(PrefillArgs a) {
         if (wide) *wide_flag = 1;
       }
       __syncthreads();                 // tile t is in LDS
+      preload_k();
       fetch(pk0, pv0, t + 2);
       compute(half_tag, t);
       __syncthreads();
@@ -451,6 +458,7 @@ void prefill_kernel(PrefillArgs a) {
       }
       __syncthreads();
       const int gave_up = kHalf ? __builtin_amdgcn_readfirstlane(*wide_flag) : 0;
+      preload_k();
       fetch(pk1, pv1, t + 3);
       compute(half_tag, t + 1);
       if (gave_up) return false;
