@@ -370,6 +370,27 @@ def test_decode_and_prefill_reject_an_empty_pool_with_work():
                              None, 0, pa.PA_BF16, None) == pa.PA_OK
 
 
+def test_cache_shape_helpers_and_mismatch_rejected():
+    """K is [N, Hkv, D/32, B, 32]; the binding reads N, Hkv, D, B from V and
+    rejects a K tensor of any other shape (the old slot-major [N, Hkv, B, D]
+    included) before calling the library."""
+    import torch
+    assert pa.k_cache_shape(10, 8, 128) == (10, 8, 4, 16, 32)
+    assert pa.v_cache_shape(10, 8, 128) == (10, 8, 128, 16)
+    vc = torch.zeros(pa.v_cache_shape(10, 8, 128), dtype=torch.float16)
+    good = torch.zeros(pa.k_cache_shape(10, 8, 128), dtype=torch.float16)
+    assert pa._cache_dims(good, vc) == (10, 8, 16, 128)
+    for bad in (torch.zeros(10, 8, 16, 128, dtype=torch.float16),
+                torch.zeros(pa.k_cache_shape(10, 8, 64), dtype=torch.float16),
+                torch.zeros(pa.k_cache_shape(11, 8, 128), dtype=torch.float16)):
+        with pytest.raises(pa.PAError):
+            pa.copy_blocks(bad, vc, torch.zeros((0, 2), dtype=torch.int32))
+    q = torch.zeros(1, 8, 128, dtype=torch.float16)
+    with pytest.raises(pa.PAError):
+        pa.decode(q.clone(), q, torch.zeros(10, 8, 16, 128, dtype=torch.float16), vc,
+                  torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 16, 0.1)
+
+
 def test_prefill_and_swap_zero_work_are_noops():
     assert pa._lib.pa_prefill_chunk(None, None, None, None, 0, None, 1, None, None, 0, 0, 0, 8, 8, 64, 16,
                                     0.1, pa.PA_FP16, None) == pa.PA_OK
