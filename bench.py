@@ -48,7 +48,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_16BIT_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
 METRIC = "paged-decode KV GB/s (% of HBM peak) + \u00b5s/step, batch 64 LLaMA-7B shape"
 FLUSH_BYTES = 512 << 20
-DECODE_SOURCES = ("paged_kv_cache_422_amd/csrc/decode.hip", "paged_kv_cache_422_amd/csrc/common.hpp")
+DECODE_SOURCES = ("paged_kv_cache_422_amd/csrc/decode.hip", "paged_kv_cache_422_amd/csrc/common.hpp",
+                  "paged_kv_cache_422_amd/csrc/launch.hpp", "paged_kv_cache_422_amd/csrc/capi.cpp")
 
 
 def parse():
@@ -767,7 +768,8 @@ def main():
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "pa_decode (partition kernel + log-sum-exp merge kernel)",
+            "kernel": "pa_decode, every kernel of one call (partition kernel, or the single-pass kernel "
+                      "when partition states are merged on chip, plus the merge pass when there is one)",
         },
         "cpu_baseline": cpu,
         "wall_ms_per_step": round(wall, 5),

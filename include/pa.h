@@ -144,17 +144,24 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
  *   scale           softmax scale (usually 1/sqrt(head_dim)).
  *   partition_size  long contexts are cut into partitions of at most this
  *                   many tokens (ceil(L / partition_size) partitions of
- *                   nearly equal size), each handled by its own workgroup,
- *                   and merged by log-sum-exp in a second kernel.  0 =
- *                   library default (pa_default_partition_size: no split when
- *                   num_seqs * num_kv_heads already gives >= 1024 work items,
- *                   else just enough split to reach that many).  Multiple of
- *                   16, <= 4096.
+ *                   nearly equal size) whose states are merged by
+ *                   log-sum-exp.  A small batch gives each partition its own
+ *                   workgroup and merges in a second kernel, through the
+ *                   workspace; a batch that already gives >= 1024 (sequence,
+ *                   KV head) work items, with head groups of at most 8 query
+ *                   heads and max_context_len <= 4096, merges on chip in a
+ *                   single pass.  0 = library default
+ *                   (pa_default_partition_size: no split when num_seqs *
+ *                   num_kv_heads already gives >= 1024 work items, else just
+ *                   enough split to reach that many).  Multiple of 16,
+ *                   <= 4096.
  *                   The result for a sequence depends only on its own data
- *                   and on the partition size, never on the rest of the batch.
+ *                   and on the partition size, never on the rest of the batch
+ *                   (both merges compute the same bits).
  *   workspace       device scratch of at least pa_decode_workspace_size()
  *                   bytes for the same arguments (may be NULL if that size is
- *                   0); contents need not be initialised.
+ *                   0; the single pass leaves it untouched); contents need not
+ *                   be initialised.
  * ---------------------------------------------------------------------- */
 int32_t   pa_default_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_context_len);

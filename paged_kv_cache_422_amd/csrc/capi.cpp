@@ -40,6 +40,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kBlock = 16;
 constexpr int kMaxPartitionTokens = 4096;   // 4 block ids per lane of a wave64
+constexpr int64_t kTargetItems = 1024;      // work items that fill the GPU (see pa_default_partition_size)
 
 pa_status check_common(const char* fn, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        pa_dtype dtype) {
@@ -74,6 +75,28 @@ int32_t decode_waves(int32_t part_blocks) {
   }();
   if (forced) return forced;
   return part_blocks >= 128 ? 8 : 4;
+}
+
+// Whether pa_decode merges a sequence's partitions on chip, in one pass, and
+// with how many wave groups per workgroup (0: two passes through the
+// workspace).  One pass needs a batch that fills the GPU without splitting
+// (so one workgroup per sequence and head group is enough work), contexts
+// whose block table fits the kernel's registers (4096 tokens) and head
+// groups of at most 8 query heads; the kernel also checks that the
+// partitions fit its LDS.  Two groups of 4 waves per workgroup measured
+// faster than one (8B-GQA shape at 512-token partitions: 403 against 418
+// us; two passes took 458).  Either way the result is the same, bit for bit.
+// PA_DECODE_FUSE (0, 1 or 2) overrides the choice for experiments; it is
+// read once per process.
+int32_t decode_fuse_groups(int64_t items, int32_t group, int32_t max_context_len) {
+  static const int32_t forced = [] {
+    const char* e = std::getenv("PA_DECODE_FUSE");
+    if (e && e[0] >= '0' && e[0] <= '2' && e[1] == '\0') return static_cast<int32_t>(e[0] - '0');
+    return static_cast<int32_t>(-1);
+  }();
+  if (group > 8 || max_context_len > kMaxPartitionTokens) return 0;
+  if (forced >= 0) return forced;
+  return items >= kTargetItems ? 2 : 0;
 }
 
 int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t num_q_heads,
@@ -184,9 +207,8 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks, void*
 // batch that already offers enough (sequence, KV head) work items to fill
 // the GPU many times over (kTargetItems) is not split at all; a smaller batch
 // is split just enough to reach that many items.  Partitions are whole
-// multiples of 16 tokens between 256 and 4096.
-constexpr int64_t kTargetItems = 1024;
-
+// multiples of 16 tokens between 256 and 4096.  (A partition size the caller
+// fixes on such a batch is merged on chip instead: decode_fuse_groups.)
 int32_t pa_default_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_context_len) {
   (void)head_dim;
@@ -279,6 +301,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_parts = static_cast<int32_t>(max_parts);
   a.max_context_len = max_context_len;
   a.waves = decode_waves(a.part_blocks);
+  a.fuse_groups = decode_fuse_groups(static_cast<int64_t>(num_seqs) * num_kv_heads * num_sub, group,
+                                     max_context_len);
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_result(fn, pa::launch_decode(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
 }

@@ -84,6 +84,152 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* k
     r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t));
 }
 
+// One 16-token block of one wave: scores, online-softmax update, P.V
+// accumulate.  n_valid (>= 1) is the number of the block's keys inside the
+// context.  Both decode kernels run exactly this code per block, so a
+// partition's state does not depend on which kernel computed it.
+template <class T, int D>
+__device__ __forceinline__ void process_block(BlockRegs<T, D>& cur, int n_valid, const u32x4 (&qb)[D / 32],
+                                              float scale_log2, int quad, float& m_run, float& l_run,
+                                              f32x4 (&o)[D / 16]) {
+  constexpr int KS = D / 32;
+  constexpr int VT = D / 16;
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) sacc = mfma16x16x32<T>(cur.k[ks], qb[ks], sacc);
+
+  float sc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    sc[e] = (4 * quad + e < n_valid) ? sacc[e] * scale_log2 : -INFINITY;
+  float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(m_run, bm);
+  const float alpha = fast_exp2(m_run - m_new);
+  uint16_t pb[4], pl[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float pe = fast_exp2(sc[e] - m_new);
+    pb[e] = from_f32<T>(pe);
+    float pr = to_f32<T>(pb[e]);
+    if constexpr (SplitP<T>::kSplit) {
+      pl[e] = from_f32<T>(pe - pr);
+      pr += to_f32<T>(pl[e]);
+    }
+    psum += pr;   // the sum uses the same rounded weights as P.V
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+
+  // Output rows are heads 4*quad + e; their rescale factors live in lanes
+  // whose column (lane % 16) is that head.
+  float ar[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * quad + e);
+
+  if (n_valid < kBlock) {
+    // Keys past the end hold stale data (possibly NaN): zero them.
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      uint32_t lo = cur.v[t][0], hi = cur.v[t][1];
+      const int k0 = 4 * quad;
+      if (k0 + 0 >= n_valid) lo &= 0xffff0000u;
+      if (k0 + 1 >= n_valid) lo &= 0x0000ffffu;
+      if (k0 + 2 >= n_valid) hi &= 0xffff0000u;
+      if (k0 + 3 >= n_valid) hi &= 0x0000ffffu;
+      cur.v[t] = u32x2{lo, hi};
+    }
+  }
+  const u32x2 pa = {pack2(pb[0], pb[1]), pack2(pb[2], pb[3])};
+  const u32x2 pal = {pack2(pl[0], pl[1]), pack2(pl[2], pl[3])};
+#pragma unroll
+  for (int t = 0; t < VT; ++t) {
+    f32x4 c = o[t];
+    c[0] *= ar[0];
+    c[1] *= ar[1];
+    c[2] *= ar[2];
+    c[3] *= ar[3];
+    c = mfma16x16x16<T>(pa, cur.v[t], c);
+    if constexpr (SplitP<T>::kSplit) c = mfma16x16x16<T>(pal, cur.v[t], c);
+    o[t] = c;
+  }
+}
+
+// The W wave states of one partition merged for head h, dimension d: the
+// partition's max M, sum and unnormalised accumulator element.
+template <int W, int NH, int D>
+__device__ __forceinline__ void merge_waves(const float (&sm_m)[W][NH], const float (&sm_l)[W][NH],
+                                            const float (&sm_o)[W][NH][D], int h, int d, float& M,
+                                            float& lsum, float& acc) {
+  M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v][h]);
+  lsum = 0.f;
+  acc = 0.f;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    const float f = fast_exp2(sm_m[v][h] - M);
+    lsum += sm_l[v][h] * f;
+    acc += sm_o[v][h][d] * f;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// The partitions of one (sequence, query head) merged by log-sum-exp, by one
+// wave: m = max_p m_p; l = sum_p l_p 2^(m_p - m); o = sum_p acc_p 2^(m_p - m)
+// / l, partitions in index order.  Partition p's (m_p, l_p) is ml[2p],
+// ml[2p + 1] and its accumulator row starts at acc + p * acc_stride.  Lane p
+// holds partition p's (m_p, l_p) (lanes take partitions p, p + 64, ... when
+// there are more than 64), so the state is read once, and the accumulator
+// loads of four partitions are in flight together.  Used by the merge pass
+// (states in the workspace) and by the single-pass kernel (states in LDS).
+template <class T, int D>
+__device__ __forceinline__ void merge_partitions(const float* ml, const float* acc, int64_t acc_stride,
+                                                 int np, int lane, uint16_t* out_row) {
+  const float m0 = lane < np ? ml[2 * lane] : -INFINITY;
+  const float l0 = lane < np ? ml[2 * lane + 1] : 0.f;
+  float M = m0;
+  for (int p = lane + 64; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
+  M = wave_max(M);
+  const float w0 = fast_exp2(m0 - M);          // weight of partition `lane`
+  float lsum = l0 * w0;
+  for (int p = lane + 64; p < np; p += 64) lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  lsum = wave_sum(lsum);
+  constexpr int PER = D / 64;
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += 4) {
+    float v[4][PER], f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + k;
+      f[k] = p >= np ? 0.f : p < 64 ? __shfl(w0, p) : fast_exp2(ml[2 * p] - M);
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        v[k][i] = p < np ? acc[static_cast<int64_t>(p) * acc_stride + lane + 64 * i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += v[k][i] * f[k];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out_row[lane + 64 * i] = from_f32<T>(o[i] / lsum);
+}
+
 // W waves share one partition (W = 4 or 8); each keeps two blocks in flight
 // in three register buffers, which fits two waves per SIMD.
 template <class T, int D, int NH, int W>
@@ -170,70 +316,8 @@ void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One 16-token block: scores, online-softmax update, P.V accumulate.
-  auto process = [&](BlockRegs<T, D>& cur, int j) {
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sacc = mfma16x16x32<T>(cur.k[ks], qb[ks], sacc);
-
-    const int n_valid = L - (blk0 + j) * kBlock;   // >= 1
-    float sc[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sc[e] = (4 * quad + e < n_valid) ? sacc[e] * a.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = fast_exp2(m_run - m_new);
-    uint16_t pb[4], pl[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pe = fast_exp2(sc[e] - m_new);
-      pb[e] = from_f32<T>(pe);
-      float pr = to_f32<T>(pb[e]);
-      if constexpr (SplitP<T>::kSplit) {
-        pl[e] = from_f32<T>(pe - pr);
-        pr += to_f32<T>(pl[e]);
-      }
-      psum += pr;   // the sum uses the same rounded weights as P.V
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // Output rows are heads 4*quad + e; their rescale factors live in lanes
-    // whose column (lane % 16) is that head.
-    float ar[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * quad + e);
-
-    if (n_valid < kBlock) {
-      // Keys past the end hold stale data (possibly NaN): zero them.
-#pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        uint32_t lo = cur.v[t][0], hi = cur.v[t][1];
-        const int k0 = 4 * quad;
-        if (k0 + 0 >= n_valid) lo &= 0xffff0000u;
-        if (k0 + 1 >= n_valid) lo &= 0x0000ffffu;
-        if (k0 + 2 >= n_valid) hi &= 0xffff0000u;
-        if (k0 + 3 >= n_valid) hi &= 0x0000ffffu;
-        cur.v[t] = u32x2{lo, hi};
-      }
-    }
-    const u32x2 pa = {pack2(pb[0], pb[1]), pack2(pb[2], pb[3])};
-    const u32x2 pal = {pack2(pl[0], pl[1]), pack2(pl[2], pl[3])};
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      f32x4 c = o[t];
-      c[0] *= ar[0];
-      c[1] *= ar[1];
-      c[2] *= ar[2];
-      c[3] *= ar[3];
-      c = mfma16x16x16<T>(pa, cur.v[t], c);
-      if constexpr (SplitP<T>::kSplit) c = mfma16x16x16<T>(pal, cur.v[t], c);
-      o[t] = c;
-    }
+  auto process = [&](BlockRegs<T, D>& cur, int j) __attribute__((always_inline)) {
+    process_block<T, D>(cur, L - (blk0 + j) * kBlock, qb, a.scale_log2, quad, m_run, l_run, o);
   };
 
   // Software pipeline over three register buffers: the loads of the next two
@@ -293,16 +377,8 @@ void decode_partition_kernel(DecodeArgs a) {
   for (int i = tid; i < nh * D; i += kThreads) {
     const int h = i / D;
     const int d = i - h * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v][h]);
-    float lsum = 0.f, acc = 0.f;
-#pragma unroll
-    for (int v = 0; v < W; ++v) {
-      const float f = fast_exp2(sm_m[v][h] - M);
-      lsum += sm_l[v][h] * f;
-      acc += sm_o[v][h][d] * f;
-    }
+    float M, lsum, acc;
+    merge_waves<W, NH, D>(sm_m, sm_l, sm_o, h, d, M, lsum, acc);
     if (poison) acc = NAN;
     const int64_t row = static_cast<int64_t>(s) * a.num_q_heads + hq0 + h;
     if (np == 1) {
@@ -318,23 +394,246 @@ void decode_partition_kernel(DecodeArgs a) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+// Single-pass split-KV: one workgroup of NGRP * W waves takes every
+// partition of one (sequence, head group) and merges them on chip, so the
+// partition states never go through HBM.  Wave group gi = w / W takes
+// partitions gi, gi + NGRP, ...; inside a partition its W waves interleave
+// the blocks exactly as the W waves of decode_partition_kernel do (wave wl
+// takes blocks start + wl, start + wl + W, ...), each wave's state goes to
+// LDS, and the states are merged with the same code as the two-pass path
+// (merge_waves, then merge_partitions).  The result is therefore bit-identical
+// to decode_partition_kernel + decode_merge_kernel at the same partition size,
+// which keeps it independent of the batch the sequence is in.  Each wave's
+// register pipeline runs on across partition boundaries.  The whole block
+// table of the sequence sits in registers (at most 64 * kBtRegs blocks) and
+// at most PMAX partitions fit in LDS; the host only picks this kernel when
+// both hold.
+template <int W, int NH, int D, int NGRP>
+constexpr int fused_max_parts() {
+  // LDS budget per workgroup: two 4-wave workgroups or one 8-wave workgroup
+  // per CU (160 KB).
+  constexpr int budget = W * NGRP <= 4 ? 78 * 1024 : 150 * 1024;
+  constexpr int per_part = (W * NH * (D + 2) + 2 * NH) * 4;
+  return budget / per_part < 32 ? budget / per_part : 32;
 }
-__device__ __forceinline__ float wave_sum(float x) {
+
+template <class T, int D, int NH, int W, int NGRP>
+__global__ __launch_bounds__(64 * W * NGRP) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_fused_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int VT = D / 16;
+  constexpr int kThreads = 64 * W * NGRP;
+  constexpr int PMAX = fused_max_parts<W, NH, D, NGRP>();
+  __shared__ float sm_m[PMAX][W][NH];
+  __shared__ float sm_l[PMAX][W][NH];
+  __shared__ float sm_o[PMAX][W][NH][D];
+  __shared__ float sm_ml[NH][PMAX][2];
+
+  // blockIdx.x = s * num_kv_heads + KV head (one head sub-group: group <= 16)
+  const int g = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.num_kv_heads));
+  const int s = static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.num_kv_heads));
+  const int hq0 = g * a.group;
+  const int nh = a.group;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gi = w / W;
+  const int wl = w - gi * W;
+  const int hl = lane & 15;
+  const int quad = lane >> 4;
+
+  const int L = a.context_lens[s];
+  const int np = num_partitions(L, a);
+  if (np <= 0) {
+    // Empty context: zero rows.  Invalid length: NaN rows.
+    const uint16_t fill = np == 0 ? uint16_t(0) : from_f32<T>(NAN);
+    for (int i = tid; i < nh * D; i += kThreads)
+      a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + i / D) * D + i % D] = fill;
+    return;
+  }
+  const int nb_seq = (L + kBlock - 1) / kBlock;   // <= 64 * kBtRegs, np <= PMAX (host)
+
+  // The sequence's block ids, 64 per register with one per lane.
+  int my_bt[kBtRegs];
+  bool bad_id = false;
+  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(s) * a.bt_stride;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+  for (int r = 0; r < kBtRegs; ++r) {
+    my_bt[r] = 0;
+    if (64 * r < nb_seq) {                    // wave-uniform
+      const int jj = 64 * r + lane;
+      if (jj < nb_seq) my_bt[r] = bt_row[jj];
+      const bool bad = jj < nb_seq && (my_bt[r] < 0 || my_bt[r] >= a.num_blocks);
+      bad_id |= bad;
+      if (bad) my_bt[r] = 0;
+    }
+  }
+  // A bad id anywhere poisons the sequence's row, as it does through the
+  // merge of the two-pass path (every wave holds the whole table).
+  const bool poison = __any(bad_id);
+
+  u32x4 qb[KS];
+  if (hl < nh) {
+    const uint16_t* qp = a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0 + hl) * D + 8 * quad;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
+  const uint16_t* vbase = a.v_cache + g * tile_elems + hl * kBlock + 4 * quad;
+
+  // Partitions this wave has no block in keep the empty state (max -inf,
+  // sum 0, accumulator 0), as the idle waves of a short partition do in the
+  // two-pass kernel.  Every slot written here belongs to this wave alone, and
+  // LDS writes of one wave land in program order, so the states stored below
+  // overwrite these.
+  for (int p = gi; p < np; p += NGRP) {
+    if (lane < NH) {
+      sm_m[p][wl][lane] = -INFINITY;
+      sm_l[p][wl][lane] = 0.f;
+    }
+    for (int i = lane; i < NH * D; i += 64) sm_o[p][wl][i / D][i % D] = 0.f;
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 o[VT];
+#pragma unroll
+  for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Lane p holds the first block of partition p (p <= np < 64).
+  const int start_lane = partition_start(min(lane, np), nb_seq, np);
+  auto pstart = [&](int p) { return __builtin_amdgcn_readlane(start_lane, p); };
+  // A cursor (p, j) is this wave's block j (absolute index in the sequence)
+  // of partition p; p >= np once the wave has no more blocks.
+  auto settle = [&](int& p, int& j) {
+    while (p < np && j >= pstart(p + 1)) {
+      p += NGRP;
+      if (p < np) j = pstart(p) + wl;
+    }
+  };
+  auto advance = [&](int& p, int& j) {
+    if (p < np) {
+      j += W;
+      settle(p, j);
+    }
+  };
+  auto blk_off = [&](int jj) {
+    const int r = jj >> 6;                    // wave-uniform
+    int id = __builtin_amdgcn_readlane(my_bt[0], jj & 63);
+#pragma unroll
+    for (int k = 1; k < kBtRegs; ++k)
+      if (r == k) id = __builtin_amdgcn_readlane(my_bt[k], jj & 63);
+    return static_cast<int64_t>(id) * blk_elems;
+  };
+  // Past the end, prefetches read block 0 of the pool, as in the two-pass kernel.
+  auto pf_off = [&](int p, int j) -> int64_t { return p < np ? blk_off(j) : int64_t(0); };
+
+  // The wave's state for partition pc goes to LDS when its first block of a
+  // later partition comes up, and after the loop.  Same store as after the
+  // loop of decode_partition_kernel.
+  int pc = -1;
+  auto flush = [&]() {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (lane < NH) {
+      sm_m[pc][wl][lane] = m_run;
+      sm_l[pc][wl][lane] = l_run;
+    }
+#pragma unroll
+    for (int t = 0; t < VT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = 4 * quad + e;
+        if (h < NH) sm_o[pc][wl][h][16 * t + hl] = o[t][e];
+      }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto process = [&](BlockRegs<T, D>& cur, int p, int j) __attribute__((always_inline)) {
+    if (p != pc) {
+      if (pc >= 0) flush();
+      pc = p;
+    }
+    process_block<T, D>(cur, L - j * kBlock, qb, a.scale_log2, quad, m_run, l_run, o);
+  };
+
+  // Three register buffers, two blocks in flight, as in the two-pass kernel;
+  // c0 is the cursor of the block being processed, c1 and c2 of the next two.
+  int p0 = gi, j0 = 0;
+  if (p0 < np) j0 = pstart(p0) + wl;
+  settle(p0, j0);
+  if (p0 < np) {
+    int p1 = p0, j1 = j0;
+    advance(p1, j1);
+    int p2 = p1, j2 = j1;
+    advance(p2, j2);
+    BlockRegs<T, D> b0, b1, b2;
+    load_block<T, D>(b0, kbase, vbase, blk_off(j0));
+    load_block<T, D>(b1, kbase, vbase, pf_off(p1, j1));
+    auto shift = [&]() {
+      p0 = p1; j0 = j1;
+      p1 = p2; j1 = j2;
+      advance(p2, j2);
+    };
+    for (;;) {
+      load_block<T, D>(b2, kbase, vbase, pf_off(p2, j2));
+      process(b0, p0, j0);
+      shift();
+      if (p0 >= np) break;
+      load_block<T, D>(b0, kbase, vbase, pf_off(p2, j2));
+      process(b1, p0, j0);
+      shift();
+      if (p0 >= np) break;
+      load_block<T, D>(b1, kbase, vbase, pf_off(p2, j2));
+      process(b2, p0, j0);
+      shift();
+      if (p0 >= np) break;
+    }
+    flush();
+  }
+  __syncthreads();
+
+  // Per partition, the W wave states merged (same code as the two-pass
+  // kernel).  A partition's accumulator replaces its wave-0 state in place:
+  // the element (p, 0, h, d) is read only by the thread that writes it.
+  for (int i = tid; i < np * nh * D; i += kThreads) {
+    const int p = i / (nh * D);
+    const int r = i - p * (nh * D);
+    const int h = r / D;
+    const int d = r - h * D;
+    float M, lsum, acc;
+    merge_waves<W, NH, D>(sm_m[p], sm_l[p], sm_o[p], h, d, M, lsum, acc);
+    if (poison) acc = NAN;
+    if (np == 1) {
+      a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + h) * D + d] = from_f32<T>(acc / lsum);
+    } else {
+      sm_o[p][0][h][d] = acc;
+      if (d == 0) {
+        sm_ml[h][p][0] = M;
+        sm_ml[h][p][1] = lsum;
+      }
+    }
+  }
+  if (np == 1) return;
+  __syncthreads();
+
+  // The partitions merged per query head, one wave per head (the merge
+  // pass's code, reading LDS instead of the workspace).
+  for (int h = w; h < nh; h += W * NGRP)
+    merge_partitions<T, D>(&sm_ml[h][0][0], &sm_o[0][0][h][0], static_cast<int64_t>(W) * NH * D, np, lane,
+                           a.out + (static_cast<int64_t>(s) * a.num_q_heads + hq0 + h) * D);
 }
 
 // Second pass: one wave per (sequence, query head) with more than one
-// partition.  m = max_p m_p; l = sum_p l_p 2^(m_p - m);
-// o = sum_p acc_p 2^(m_p - m) / l, partitions in index order.  Lane p holds
-// partition p's (m_p, l_p) (lanes take partitions p, p + 64, ... when there
-// are more than 64), so the state is read once, and the accumulator loads of
-// four partitions are in flight together.
+// partition, merging the partition states of the workspace.
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -343,42 +642,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int s = static_cast<int>(row / a.num_q_heads);
   const int np = num_partitions(a.context_lens[s], a);
   if (np <= 1) return;
-  const float* ml = a.ws_ml + row * a.max_parts * 2;
-  const float* acc = a.ws_acc + row * a.max_parts * D;
-  const float m0 = lane < np ? ml[2 * lane] : -INFINITY;
-  const float l0 = lane < np ? ml[2 * lane + 1] : 0.f;
-  float M = m0;
-  for (int p = lane + 64; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-  const float w0 = fast_exp2(m0 - M);          // weight of partition `lane`
-  float lsum = l0 * w0;
-  for (int p = lane + 64; p < np; p += 64) lsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-  lsum = wave_sum(lsum);
-  constexpr int PER = D / 64;
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += 4) {
-    float v[4][PER], f[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = p0 + k;
-      f[k] = p >= np ? 0.f : p < 64 ? __shfl(w0, p) : fast_exp2(ml[2 * p] - M);
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        v[k][i] = p < np ? acc[static_cast<int64_t>(p) * D + lane + 64 * i] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += v[k][i] * f[k];
+  merge_partitions<T, D>(a.ws_ml + row * a.max_parts * 2, a.ws_acc + row * a.max_parts * D, D, np, lane,
+                         a.out + row * D);
+}
+
+template <class T, int D, int NH, int W, int NGRP>
+bool launch_fused(const DecodeArgs& a, hipStream_t stream) {
+  if (a.max_parts > fused_max_parts<W, NH, D, NGRP>()) return false;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_kv_heads));
+  hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, W, NGRP>), grid, dim3(64 * W * NGRP), 0, stream, a);
+  return true;
+}
+
+// The single-pass kernel, when the host chose it (fuse_groups > 0: the batch
+// fills the GPU without splitting, a sequence's table fits the registers and
+// a head group is at most 8 query heads) and the partitions fit its LDS.
+template <class T, int D, int NH>
+bool try_fused(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (NH > 8) {
+    return false;
+  } else {
+    if (a.fuse_groups <= 0 || a.max_parts <= 1 || a.num_sub != 1) return false;
+    if (a.waves == 8) return launch_fused<T, D, NH, 8, 1>(a, stream);
+    if (a.fuse_groups == 2) return launch_fused<T, D, NH, 4, 2>(a, stream);
+    return launch_fused<T, D, NH, 4, 1>(a, stream);
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) a.out[row * D + lane + 64 * i] = from_f32<T>(o[i] / lsum);
 }
 
 template <class T, int D, int NH>
 hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
+  if (try_fused<T, D, NH>(a, stream)) return hipGetLastError();
   const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
   const dim3 grid(static_cast<uint32_t>(n_wg));
   if (a.waves == 8)

@@ -141,6 +141,41 @@ def test_batch_invariance_is_bit_exact():
         assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16))
 
 
+# A batch of at least 1024 (sequence, KV head) work items runs the single-pass
+# kernel (partition states merged in LDS); one sequence alone runs the
+# two-pass kernels (partition states through the workspace).  Both must give
+# the same bits.  Cases: bf16 GQA at the 8B workload's 512-token partitions
+# (4-wave groups), fp16 MHA at 256-token partitions, bf16 GQA at 2048-token
+# partitions (8-wave groups).
+@pytest.mark.parametrize("dtype,S,Hq,Hkv,P,max_len", [
+    (torch.bfloat16, 128, 32, 8, 512, 4096),
+    (torch.float16, 32, 32, 32, 256, 2048),
+    (torch.bfloat16, 128, 32, 8, 2048, 4096),
+], ids=["bf16-gqa-P512", "fp16-mha-P256", "bf16-gqa-P2048"])
+def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, P, max_len):
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, max_len + 1, S)
+    # edges: one block, a partition exactly, one key past it, the maximum,
+    # and an odd number of partitions
+    lens[:6] = [1, 16, P, P + 1, max_len, min(3 * P - 5, max_len - 3)]
+    q, kc, vc, bt, ctx = small_case(S, Hq, Hkv, 128, dtype, lens, seed=22, extra_blocks=8)
+    print(f"single pass: S={S} Hq={Hq} Hkv={Hkv} P={P} blocks={kc.shape[0]}", flush=True)
+    full = run_decode(q, kc, vc, bt, ctx, max_len, 0.088, P)
+    for s in range(8):
+        one = run_decode(q[s:s + 1].contiguous(), kc, vc, bt[s:s + 1], ctx[s:s + 1], max_len, 0.088, P)
+        assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16)), f"sequence {s}"
+    seqs = list(range(8)) + [int(x) for x in rng.choice(np.arange(8, S), 8, replace=False)]
+    want = oracle_decode(q, kc, vc, bt, ctx, 0.088, seqs=seqs)
+    assert_close(full[seqs], want[seqs], what="single pass vs oracle")
+    # an out-of-range block id poisons only its own sequence's rows
+    bt2 = bt.copy()
+    bt2[3, 0] = kc.shape[0] + 7
+    bad = run_decode(q, kc, vc, bt2, ctx, max_len, 0.088, P).float().cpu().numpy()
+    assert np.all(np.isnan(bad[3]))
+    keep = [s for s in range(S) if s != 3]
+    assert np.array_equal(bad[keep], full.float().cpu().numpy()[keep])
+
+
 def test_partition_size_changes_only_rounding():
     lens = [2000, 1500, 999]
     q, kc, vc, bt, ctx = small_case(3, 8, 8, 128, torch.float16, lens, seed=14)
