@@ -201,7 +201,7 @@ def cpu_oracle_decode(q, kc, vc, block_tables, context_lens, scale, dtype, budge
     order = list(range(len(context_lens))) if seqs is None else list(seqs)
     per_seq = {}
     qh = bits(q)
-    Hkv, D = vc.shape[1], vc.shape[2]
+    Hkv, D = vc.shape[1], vc.shape[3]
     t0 = time.perf_counter()
     c0 = time.process_time()
     done = bytes_done = 0
@@ -233,7 +233,7 @@ def build_shared_cache(torch, pa, w, k_tok, v_tok):
     pool = pa.BlockPool(w.num_blocks, 16, 7)
     H, D = w.num_kv_heads, w.head_dim
     kc = torch.zeros(pa.k_cache_shape(w.num_blocks, H, D), dtype=k_tok.dtype, device="cuda")
-    vc = torch.zeros((w.num_blocks, H, D, 16), dtype=k_tok.dtype, device="cuda")
+    vc = torch.zeros(pa.v_cache_shape(w.num_blocks, H, D), dtype=k_tok.dtype, device="cuda")
     seqs = [None] * w.num_seqs
 
     def write(i, sid, lo, hi):
@@ -277,7 +277,7 @@ def bench_prefix_cache(args, np, torch, pa):
     g = torch.Generator(device="cuda").manual_seed(4230)
     dt = torch.bfloat16
     kc = torch.randn(pa.k_cache_shape(num_blocks, Hkv, D, B), generator=g, device="cuda").to(dt)
-    vc = torch.randn(num_blocks, Hkv, D, B, generator=g, device="cuda").to(dt)
+    vc = torch.randn(pa.v_cache_shape(num_blocks, Hkv, D, B), generator=g, device="cuda").to(dt)
 
     def admit(caching):
         pool = pa.BlockPool(num_blocks, B, 4230, prefix_caching=caching)
@@ -365,9 +365,9 @@ def bench_swap(args, np, torch, pa):
     g = torch.Generator(device="cuda").manual_seed(4231)
     dt = torch.bfloat16
     kc = torch.randn(pa.k_cache_shape(N, H, D, B), generator=g, device="cuda").to(dt)
-    vc = torch.randn(N, H, D, B, generator=g, device="cuda").to(dt)
+    vc = torch.randn(pa.v_cache_shape(N, H, D, B), generator=g, device="cuda").to(dt)
     hk = torch.empty(pa.k_cache_shape(NH, H, D, B), dtype=dt).pin_memory()
-    hv = torch.empty(NH, H, D, B, dtype=dt).pin_memory()
+    hv = torch.empty(pa.v_cache_shape(NH, H, D, B), dtype=dt).pin_memory()
     out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], 1)).cuda()
     in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], 1)).cuda()
     nbytes = NSW * 2 * H * B * D * 2
@@ -424,7 +424,7 @@ def bench_beam(args, np, torch, pa):
     g = torch.Generator(device="cuda").manual_seed(4232)
     dt = torch.bfloat16
     kc = torch.randn(pa.k_cache_shape(N, Hkv, D, B), generator=g, device="cuda").to(dt)
-    vc = torch.randn(N, Hkv, D, B, generator=g, device="cuda").to(dt)
+    vc = torch.randn(pa.v_cache_shape(N, Hkv, D, B), generator=g, device="cuda").to(dt)
     pool = pa.BlockPool(N, B, 4232)
     beams = []
     for _ in range(R):

@@ -30,15 +30,20 @@
  *
  * KV cache storage (one pair of tensors per layer, caller-allocated):
  *   k_cache  [num_blocks][num_kv_heads][head_dim / 32][block_size][32]
- *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
+ *   v_cache  [num_blocks][num_kv_heads][block_size / 4][head_dim][4]
  * Token t of a sequence lives in block block_table[t / block_size], slot
  * t % block_size; its storage address ("slot") is block * block_size + slot.
  * Element d of a key sits in 32-dim chunk d / 32 at position d % 32 of its
- * slot's 64-byte row.  One (block, kv head) tile is contiguous in both
- * tensors (4 KiB at D = 128).  The layouts serve the matrix-core operands of
- * the attention kernels: one load of the K operand for a 32-dim step reads a
- * whole contiguous 1 KiB chunk (16 keys x 32 dims), and V is stored dim-major
- * because the P.V operands run along the key index.
+ * slot's 64-byte row; element d of a value in slot s sits at [s / 4][d][s % 4]
+ * (groups of four slots, dim-major within a group).  One (block, kv head)
+ * tile is contiguous in both tensors (4 KiB at D = 128).  The layouts serve
+ * the matrix-core operands of the attention kernels: one load of the K
+ * operand for a 32-dim step reads a whole contiguous 1 KiB chunk (16 keys x
+ * 32 dims), and a P.V operand (four consecutive keys of one dim) is one
+ * 8-byte piece of V.  A single new token's values then fill a quarter of each
+ * 32-byte sector they touch (D / 4 sectors per head) instead of 2 bytes of
+ * each of D sectors, which keeps the memory's read-modify-write of partly
+ * written sectors small when decode tokens are written.
  *
  * Device data (block ids, slots, context lengths) is checked inside the
  * kernels: an out-of-range slot or pair is skipped by the write and copy

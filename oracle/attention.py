@@ -11,7 +11,7 @@ only "fixed-size blocks" of 16 tokens by default, [IV §PagedAttention: What the
 OS Figured Out Decades Ago]):
 
     k_cache[block, kv_head, dim // 32, slot, dim % 32]   shape [N, Hkv, D/32, B, 32]
-    v_cache[block, kv_head, dim, slot]                   shape [N, Hkv, D, B]
+    v_cache[block, kv_head, slot // 4, dim, slot % 4]    shape [N, Hkv, B/4, D, 4]
 
 Token t of a sequence with block-table row ``bt`` lives in block
 ``bt[t // B]`` at slot ``t % B``.
@@ -67,10 +67,11 @@ def gather_kv(k_cache: np.ndarray, v_cache: np.ndarray, bt_row, n_tokens: int,
     """
     n_blocks = -(-n_tokens // block_size)
     phys = np.asarray(bt_row[:n_blocks], dtype=np.int64)
-    D = v_cache.shape[2]
+    D = v_cache.shape[3]
     k_raw = k_cache[phys, kv_head].transpose(0, 2, 1, 3).reshape(len(phys), block_size, D)
     # [nb, D/32, B, 32] -> [nb, B, D/32, 32] -> [nb, B, D]
-    v_raw = v_cache[phys, kv_head].transpose(0, 2, 1)  # [nb, D, B] -> [nb, B, D]
+    v_raw = v_cache[phys, kv_head].transpose(0, 1, 3, 2).reshape(len(phys), block_size, D)
+    # [nb, B/4, D, 4] -> [nb, B/4, 4, D] -> [nb, B, D]
     K = widen(np.ascontiguousarray(k_raw), dtype).reshape(-1, D)[:n_tokens]
     V = widen(np.ascontiguousarray(v_raw), dtype).reshape(-1, D)[:n_tokens]
     return K, V

@@ -15,7 +15,9 @@ is a whole-block duplicate of K and V for every KV head.
 Operates in place on raw 16-bit patterns (numpy uint16 or float16), so the
 result is compared bit for bit.  Storage format (the library's documented
 one): k_cache [N, Hkv, D/32, B, 32] (element d of the key in slot s at
-[.., d // 32, s, d % 32]), v_cache [N, Hkv, D, B] (dim-major).
+[.., d // 32, s, d % 32]), v_cache [N, Hkv, B/4, D, 4] (groups of four
+slots, dim-major within a group: element d of the value in slot s at
+[.., s // 4, d, s % 4]).
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
         blk, off = divmod(int(slot), block_size)
         H, D = k[i].shape
         k_cache[blk, :, :, off, :] = k[i].reshape(H, D // 32, 32)
-        v_cache[blk, :, :, off] = v[i]
+        v_cache[blk, :, off // 4, :, off % 4] = v[i]
 
 
 def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> None:

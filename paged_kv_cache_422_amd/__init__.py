@@ -9,8 +9,9 @@ calls ``__graft_entry__.build()``).
 Function names and arguments follow include/pa.h.  Cache tensors use the
 library's storage format (``k_cache_shape`` / ``v_cache_shape``):
     k_cache [num_blocks, num_kv_heads, head_dim // 32, 16, 32]
-    v_cache [num_blocks, num_kv_heads, head_dim, 16]
-Element d of a key sits in 32-dim chunk d // 32 at position d % 32.
+    v_cache [num_blocks, num_kv_heads, 4, head_dim, 4]
+Element d of a key sits in 32-dim chunk d // 32 at position d % 32; element
+d of the value in slot s sits at [s // 4, d, s % 4].
 """
 from __future__ import annotations
 
@@ -134,13 +135,17 @@ def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size:
 
 
 def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = 16):
-    """Shape of a V cache tensor: dim-major within a block."""
-    return (num_blocks, num_kv_heads, head_dim, block_size)
+    """Shape of a V cache tensor: groups of four slots, dim-major within a group."""
+    return (num_blocks, num_kv_heads, block_size // 4, head_dim, 4)
 
 
 def _cache_dims(k_cache, v_cache):
     """(num_blocks, num_kv_heads, block_size, head_dim) of a K/V cache pair."""
-    N, H, D, B = v_cache.shape
+    if v_cache.dim() != 5 or v_cache.shape[4] != 4:
+        raise PAError(PA_EINVAL, f"v_cache shape {tuple(v_cache.shape)} is not "
+                                 "[num_blocks, num_kv_heads, block_size // 4, head_dim, 4]")
+    N, H, G, D, _ = v_cache.shape
+    B = 4 * G
     if D % 32 or tuple(k_cache.shape) != k_cache_shape(N, H, D, B):
         raise PAError(PA_EINVAL, f"k_cache shape {tuple(k_cache.shape)} does not match "
                                  f"v_cache {tuple(v_cache.shape)}: expected {k_cache_shape(N, H, D, B)}")

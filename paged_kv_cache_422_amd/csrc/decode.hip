@@ -38,7 +38,9 @@
 //   O[16 heads x D] += P[16 x 16 keys] . V[16 keys x D]  (D/16 MFMA 16x16x16)
 // The accumulator layout of the first product is exactly the operand layout
 // the second needs for P, so probabilities never leave registers.  V is stored
-// dim-major per block, which makes the V operand an 8-byte load per lane.
+// in groups of four keys per dimension ([key / 4][dim][key % 4] per block),
+// which makes the V operand (four consecutive keys of one dimension) an
+// 8-byte load per lane.
 // Query-head columns beyond the group size are zero padding.
 #include <math.h>
 
@@ -67,7 +69,7 @@ __device__ __forceinline__ int partition_start(int p, int nb, int np) {
 template <class T, int D>
 struct BlockRegs {
   u32x4 k[D / 32];   // K: key lane%16, dims 32*ks + 8*(lane/16) .. +7 (chunk ks)
-  u32x2 v[D / 16];   // V: dim 16*t + lane%16, keys 4*(lane/16) .. +3
+  u32x2 v[D / 16];   // V: dim 16*t + lane%16, keys 4*(lane/16) .. +3 (key group lane/16)
 };
 
 template <class T, int D>
@@ -75,13 +77,13 @@ __device__ __forceinline__ void load_block(BlockRegs<T, D>& r, const uint16_t* k
                                            const uint16_t* vbase, int64_t off) {
   // K and V are read once per step: non-temporal loads.  Each covers whole
   // 128-byte lines: a K load one 1 KiB chunk (16 keys x 32 dims), a V load
-  // 16 dims x 16 keys x 2 bytes = 512 contiguous bytes.
+  // 16 dims x 4 keys x 2 bytes = one line in each of the four key groups.
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     r.k[ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + kBlock * 32 * ks));
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
-    r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vbase + off + 16 * kBlock * t));
+    r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vbase + off + 16 * 4 * t));
 }
 
 // One 16-token block of one wave: scores, online-softmax update, P.V
@@ -308,7 +310,7 @@ void decode_partition_kernel(DecodeArgs a) {
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
   const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
-  const uint16_t* vbase = a.v_cache + g * tile_elems + hl * kBlock + 4 * quad;
+  const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
 
   float m_run = -INFINITY;   // running max of this lane's head (log2 units)
   float l_run = 0.f;         // this lane's share of the running sum
@@ -485,7 +487,7 @@ void decode_fused_kernel(DecodeArgs a) {
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
   const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
-  const uint16_t* vbase = a.v_cache + g * tile_elems + hl * kBlock + 4 * quad;
+  const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
 
   // Partitions this wave has no block in keep the empty state (max -inf,
   // sum 0, accumulator 0), as the idle waves of a short partition do in the

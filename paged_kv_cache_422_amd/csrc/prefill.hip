@@ -37,9 +37,11 @@
 // lane l (half h = l / 32) holds key 16 * (i / 8) + 8 * h + i % 8: the eight
 // probabilities a lane feeds to the P.V step for 16 keys are its own eight
 // consecutive accumulator elements, and the matching V^T operand is eight
-// consecutive keys of one dimension, i.e. 16 contiguous bytes of the
-// dim-major V block.  LDS rows are padded by 16 bytes so that the 16-byte
-// operand reads of a wave hit distinct banks.  Each XCD takes a contiguous
+// consecutive keys of one dimension, i.e. 16 contiguous bytes of that
+// dimension's LDS row (V is staged as one row of 16 keys per dimension; the
+// cache holds it in groups of four keys, [key / 4][dim][key % 4]).  LDS rows
+// are padded by 16 bytes so that the 16-byte operand reads of a wave hit
+// distinct banks.  Each XCD takes a contiguous
 // run of row blocks of one chunk and head group (so they share its L2), and
 // within it row blocks are dispatched heaviest (longest causal range) first.
 #include <float.h>
@@ -241,18 +243,22 @@ void prefill_kernel(PrefillArgs a) {
       const bool live = t * kTileBlocks + b < nb_seq;
       *reinterpret_cast<u32x4*>(lds + row * Lds::kRow + ((wu >> 6) * 4 + (wu & 3)) * 16) =
           live ? pk[r] : u32x4{0, 0, 0, 0};
-      const int dim = wu >> 1;
-      const int h16 = wu & 1;
+      // V unit wu is 16 bytes of key group kg = wu / (D/2): dims d0 and
+      // d0 + 1 (d0 = 2 * (wu % (D/2))), keys 4*kg .. +3 of each; dword e holds
+      // dim d0 + e/2, keys 4*kg + 2*(e%2) and the next.
+      const int kg = wu / (D / 2);
+      const int d0 = 2 * (wu % (D / 2));
       u32x4 v = pv[r];
-      const int n_ok = L - ((t * kTileBlocks + b) * kBlock + 8 * h16);   // keys of these 8 in range
+      const int n_ok = L - ((t * kTileBlocks + b) * kBlock + 4 * kg);   // keys of this group in range
       if (n_ok <= 0) {
         v = u32x4{0, 0, 0, 0};
-      } else if (n_ok < 8) {
+      } else if (n_ok < 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const int k = 2 * (e & 1);
           uint32_t x = v[e];
-          if (2 * e >= n_ok) x &= 0xffff0000u;
-          if (2 * e + 1 >= n_ok) x &= 0x0000ffffu;
+          if (k >= n_ok) x &= 0xffff0000u;
+          if (k + 1 >= n_ok) x &= 0x0000ffffu;
           v[e] = x;
         }
       }
@@ -269,7 +275,9 @@ void prefill_kernel(PrefillArgs a) {
         }
         wide |= max(mag[0], mag[1]) > 0x477f;   // bf16 bits of 65280, the largest below 65504
       }
-      *reinterpret_cast<u32x4*>(lds + Lds::kBytesK + b * Lds::kBytesVBlock + dim * Lds::kVRow + h16 * 16) = v;
+      unsigned char* const vrow = lds + Lds::kBytesK + b * Lds::kBytesVBlock + d0 * Lds::kVRow + kg * 8;
+      *reinterpret_cast<u32x2*>(vrow) = u32x2{v[0], v[1]};
+      *reinterpret_cast<u32x2*>(vrow + Lds::kVRow) = u32x2{v[2], v[3]};
     }
   };
 

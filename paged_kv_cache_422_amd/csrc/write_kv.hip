@@ -8,8 +8,9 @@
 // move raw 16-bit patterns, so they are dtype-agnostic and bit-exact.
 //
 // Storage: k_cache [N][Hkv][D/32][16][32] (32-dim chunks, slot-major within
-// a chunk), v_cache [N][Hkv][D][16] (dim-major).  HBM-bound: each token moves
-// 2 * Hkv * D * 2 bytes in and the same out.
+// a chunk), v_cache [N][Hkv][4][D][4] (groups of four slots, dim-major within
+// a group: slot s of dim d at [s / 4][d][s % 4]).  HBM-bound: each token
+// moves 2 * Hkv * D * 2 bytes in and the same out.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,15 +26,19 @@ constexpr int kBlock = 16;   // tokens per KV block
 // dims 8c .. 8c+7, which sit in 32-dim chunk c / 4 at slot i, piece c % 4.
 // A wave's 64 threads cover one whole 1 KiB chunk of 16 slots, and a decode
 // token (alone in its block) writes four whole 64-byte pieces.
-// V: a V row of a block is the 16 slots of one dim (32 bytes), so a single
-// token only touches 2 bytes of it.  The group's values pass through LDS,
-// transposed to [dim][token]; thread (dim d, half h) then owns tokens
-// 8h .. 8h+7 of dim d.  When those eight tokens go to eight consecutive slots
-// starting at a multiple of 8 (prefill chunks fill their blocks in order) the
-// thread stores them as one 16-byte piece, and its neighbour (the other half)
-// completes the 32-byte row in the same instruction, so HBM sees whole
-// sectors.  Any other mapping (decode tokens, each alone in its block, or
-// skipped tokens) falls back to one 2-byte store per token.
+// V: a token's values sit 8 bytes apart (one 2-byte piece per dim in its
+// slot group), so a single token only fills a quarter of each 32-byte sector
+// it touches: D / 4 sectors per head, where a dim-major [D][16] block would
+// touch D of them.  HBM3E has no write mask, so each partly written sector
+// costs the memory a read-modify-write; fewer sectors per token is what makes
+// the decode tokens' writes cheaper.  The group's values pass through LDS,
+// transposed to [dim][token]; thread (key group kg, dim pair d0) then owns
+// tokens 4kg .. 4kg+3 of dims d0 and d0 + 1.  When those four tokens go to
+// four consecutive slots starting at a multiple of 4 (prefill chunks fill
+// their blocks in order) the thread stores them as one 16-byte piece, and the
+// 64 threads of a wave complete whole lines.  Any other mapping (decode
+// tokens, each alone in its block, or skipped tokens) falls back to one
+// 2-byte store per token and dim.
 template <int D>
 __global__ __launch_bounds__(2 * D) void write_kv_kernel(WriteKvArgs a) {
   __shared__ int64_t slot_s[kBlock];
@@ -80,25 +85,29 @@ __global__ __launch_bounds__(2 * D) void write_kv_kernel(WriteKvArgs a) {
     }
   }
 
-  const int d = tid >> 1;
-  const int h = tid & 1;
-  const int64_t s0 = slot_s[8 * h];
-  bool run = s0 >= 0 && (s0 & 7) == 0;
+  const int kg = tid / (D / 2);        // group of four tokens
+  const int d0 = 2 * (tid % (D / 2));  // first of two dims
+  const int64_t s0 = slot_s[4 * kg];
+  bool run = s0 >= 0 && (s0 & 3) == 0;
 #pragma unroll
-  for (int j = 1; j < 8; ++j) run = run && slot_s[8 * h + j] == s0 + j;
+  for (int j = 1; j < 4; ++j) run = run && slot_s[4 * kg + j] == s0 + j;
+  const uint16_t* const vt0 = &vt[d0 * kBlock + 4 * kg];   // 4 tokens of dim d0
+  const uint16_t* const vt1 = vt0 + kBlock;                 // and of dim d0 + 1
   if (run) {
     const int64_t blk = s0 / kBlock;
-    const int off = static_cast<int>(s0 - blk * kBlock);        // 0 or 8
-    *reinterpret_cast<u32x4*>(a.v_cache + blk * blk_elems + head_tile + d * kBlock + off) =
-        *reinterpret_cast<const u32x4*>(&vt[d * kBlock + 8 * h]);
+    const int grp = static_cast<int>(s0 - blk * kBlock) / 4;
+    *reinterpret_cast<u32x4*>(a.v_cache + blk * blk_elems + head_tile + (grp * D + d0) * 4) =
+        u32x4{pack2(vt0[0], vt0[1]), pack2(vt0[2], vt0[3]), pack2(vt1[0], vt1[1]), pack2(vt1[2], vt1[3])};
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t sl = slot_s[8 * h + j];
+    for (int j = 0; j < 4; ++j) {
+      const int64_t sl = slot_s[4 * kg + j];
       if (sl < 0) continue;
       const int64_t blk = sl / kBlock;
       const int off = static_cast<int>(sl - blk * kBlock);
-      a.v_cache[blk * blk_elems + head_tile + d * kBlock + off] = vt[d * kBlock + 8 * h + j];
+      uint16_t* const dst = a.v_cache + blk * blk_elems + head_tile + ((off >> 2) * D + d0) * 4 + (off & 3);
+      dst[0] = vt0[j];
+      dst[4] = vt1[j];
     }
   }
 }

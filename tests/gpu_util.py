@@ -42,6 +42,13 @@ def assert_close(got: torch.Tensor, want: np.ndarray, mask=None, what=""):
     return float(np.max(err / bound)) if err.size else 0.0
 
 
+def set_v_slots(vc, blk: int, first: int, value) -> None:
+    """Slots first .. 15 of V cache block blk (every head and dim) set to
+    value; the library keeps slot s of dim d at [.., s // 4, d, s % 4]."""
+    for s in range(first, 4 * vc.shape[2]):
+        vc[blk, :, s // 4, :, s % 4] = value
+
+
 def run_decode(q, kc, vc, bt, ctx, max_ctx, scale, partition_size=0):
     bt_t = torch.as_tensor(bt, dtype=torch.int32).to(q.device)
     ctx_t = torch.as_tensor(ctx, dtype=torch.int32).to(q.device)

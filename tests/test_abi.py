@@ -371,12 +371,14 @@ def test_decode_and_prefill_reject_an_empty_pool_with_work():
 
 
 def test_cache_shape_helpers_and_mismatch_rejected():
-    """K is [N, Hkv, D/32, B, 32]; the binding reads N, Hkv, D, B from V and
-    rejects a K tensor of any other shape (the old slot-major [N, Hkv, B, D]
-    included) before calling the library."""
+    """K is [N, Hkv, D/32, B, 32] and V [N, Hkv, B/4, D, 4]; the binding reads
+    N, Hkv, D, B from V and rejects a K tensor of any other shape (the old
+    slot-major [N, Hkv, B, D] included), and a V tensor that is not in groups
+    of four slots (the old dim-major [N, Hkv, D, B]), before calling the
+    library."""
     import torch
     assert pa.k_cache_shape(10, 8, 128) == (10, 8, 4, 16, 32)
-    assert pa.v_cache_shape(10, 8, 128) == (10, 8, 128, 16)
+    assert pa.v_cache_shape(10, 8, 128) == (10, 8, 4, 128, 4)
     vc = torch.zeros(pa.v_cache_shape(10, 8, 128), dtype=torch.float16)
     good = torch.zeros(pa.k_cache_shape(10, 8, 128), dtype=torch.float16)
     assert pa._cache_dims(good, vc) == (10, 8, 16, 128)
@@ -389,6 +391,9 @@ def test_cache_shape_helpers_and_mismatch_rejected():
     with pytest.raises(pa.PAError):
         pa.decode(q.clone(), q, torch.zeros(10, 8, 16, 128, dtype=torch.float16), vc,
                   torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 16, 0.1)
+    with pytest.raises(pa.PAError):
+        pa.copy_blocks(good, torch.zeros(10, 8, 128, 16, dtype=torch.float16),
+                       torch.zeros((0, 2), dtype=torch.int32))
 
 
 def test_prefill_and_swap_zero_work_are_noops():

@@ -32,7 +32,7 @@ def test_beam_trace_decodes_each_beams_history(dtype):
     k_rows = torch.randn(total_rows, H, D, generator=g, device=DEV).to(dtype)
     v_rows = torch.randn(total_rows, H, D, generator=g, device=DEV).to(dtype)
     kc = torch.full(pa.k_cache_shape(N, H, D), float("nan"), dtype=dtype, device=DEV)
-    vc = torch.full((N, H, D, 16), float("nan"), dtype=dtype, device=DEV)
+    vc = torch.full(pa.v_cache_shape(N, H, D), float("nan"), dtype=dtype, device=DEV)
     pool = pa.BlockPool(N, 16, 5)
     next_row = 0
 

@@ -9,7 +9,7 @@ import torch
 
 import paged_kv_cache_422_amd as pa
 from oracle import attention as A
-from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode
+from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode, set_v_slots
 from workloads import llama7b, llama8b_gqa, tiny
 
 pytestmark = pytest.mark.gpu
@@ -35,12 +35,12 @@ def small_case(S, Hq, Hkv, D, dtype, lens, seed=0, extra_blocks=4):
     g = torch.Generator(device=DEV).manual_seed(seed)
     q = torch.randn(S, Hq, D, generator=g, device=DEV).to(dtype)
     kc = torch.randn(pa.k_cache_shape(N, Hkv, D), generator=g, device=DEV).to(dtype)
-    vc = torch.randn(N, Hkv, D, 16, generator=g, device=DEV).to(dtype)
+    vc = torch.randn(pa.v_cache_shape(N, Hkv, D), generator=g, device=DEV).to(dtype)
     # poison every slot no sequence owns
     for s, L in enumerate(lens):
         if L % 16:
             kc[int(bt[s, nb[s] - 1]), :, :, L % 16:, :] = float("nan")
-            vc[int(bt[s, nb[s] - 1]), :, :, L % 16:] = float("nan")
+            set_v_slots(vc, int(bt[s, nb[s] - 1]), L % 16, float("nan"))
     for b in perm[at:]:
         kc[int(b)] = float("nan")
         vc[int(b)] = float("nan")

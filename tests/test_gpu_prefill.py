@@ -9,7 +9,7 @@ import torch
 import paged_kv_cache_422_amd as pa
 from oracle import attention as A
 from oracle import kv_cache as KC
-from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode
+from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode, set_v_slots
 from workloads import mixed
 
 pytestmark = pytest.mark.gpu
@@ -32,11 +32,11 @@ def prefill_case(chunks, Hq, Hkv, D, dtype, seed=0):
     T = sum(n for _, n in chunks)
     q = torch.randn(T, Hq, D, generator=g, device=DEV).to(dtype)
     kc = torch.randn(pa.k_cache_shape(N, Hkv, D), generator=g, device=DEV).to(dtype)
-    vc = torch.randn(N, Hkv, D, 16, generator=g, device=DEV).to(dtype)
+    vc = torch.randn(pa.v_cache_shape(N, Hkv, D), generator=g, device=DEV).to(dtype)
     for c, L in enumerate(lens):
         if L % 16:
             kc[int(bt[c, nb[c] - 1]), :, :, L % 16:, :] = float("nan")
-            vc[int(bt[c, nb[c] - 1]), :, :, L % 16:] = float("nan")
+            set_v_slots(vc, int(bt[c, nb[c] - 1]), L % 16, float("nan"))
     for b in perm[at:]:
         kc[int(b)] = float("nan")
         vc[int(b)] = float("nan")
@@ -99,8 +99,8 @@ def test_prefill_bf16_values_beyond_fp16_range():
     for c, val in ((0, 2.0e5), (1, 65280.0)):
         for pos in (3, 57, int(lens[c]) - 2):
             blk = int(bt[c, pos // 16])
-            vc[blk, :, 5:9, pos % 16] = val
-            vc[blk, :, 100, pos % 16] = -val
+            vc[blk, :, (pos % 16) // 4, 5:9, pos % 4] = val
+            vc[blk, :, (pos % 16) // 4, 100, pos % 4] = -val
     out = run_prefill(q, kc, vc, bt, qsl, lens, 0.088)
     want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, 0.088, dtype_name(q))
     assert_close(out, want, what="prefill wide values")

@@ -42,7 +42,7 @@ def test_cached_prefix_serves_prefill_and_decode(dtype):
     pool = pa.BlockPool(N, B, 9, prefix_caching=True)
     model = PrefixKV(H, D, dtype, 3)
     kc = torch.full(pa.k_cache_shape(N, H, D, B), float("nan"), dtype=dtype, device=DEV)
-    vc = torch.full((N, H, D, B), float("nan"), dtype=dtype, device=DEV)
+    vc = torch.full(pa.v_cache_shape(N, H, D, B), float("nan"), dtype=dtype, device=DEV)
 
     def admit(tokens):
         sid = pool.create()
@@ -71,7 +71,7 @@ def test_cached_prefix_serves_prefill_and_decode(dtype):
     v_priv = torch.zeros(nb * B, H, D, dtype=dtype, device=DEV)
     k_priv[:L], v_priv[:L] = k_log, v_log
     kc_log = k_priv.view(nb, B, H, D // 32, 32).permute(0, 2, 3, 1, 4).contiguous()   # [nb, H, D/32, B, 32]
-    vc_log = v_priv.view(nb, B, H, D).permute(0, 2, 3, 1).contiguous()
+    vc_log = v_priv.view(nb, B // 4, 4, H, D).permute(0, 3, 1, 4, 2).contiguous()              # [nb, H, B/4, D, 4]
     bt_log = np.arange(nb, dtype=np.int32)[None, :]
     bt = np.array([tab], dtype=np.int32)
 

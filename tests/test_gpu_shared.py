@@ -21,7 +21,7 @@ def build_cache(w, k_tok, v_tok, share: bool, seed: int):
     pool = pa.BlockPool(w.num_blocks, 16, seed)
     H, D = w.num_kv_heads, w.head_dim
     kc = torch.full(pa.k_cache_shape(w.num_blocks, H, D), float("nan"), dtype=k_tok.dtype, device=DEV)
-    vc = torch.full((w.num_blocks, H, D, 16), float("nan"), dtype=k_tok.dtype, device=DEV)
+    vc = torch.full(pa.v_cache_shape(w.num_blocks, H, D), float("nan"), dtype=k_tok.dtype, device=DEV)
     seqs = [None] * w.num_seqs
     n_cow = 0
 

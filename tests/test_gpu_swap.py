@@ -26,8 +26,8 @@ def test_swap_blocks_bit_exact_both_ways(dtype, H, D):
     g = torch.Generator(device=DEV).manual_seed(12)
     N, NH = 20, 9
     kc = torch.randn(pa.k_cache_shape(N, H, D), generator=g, device=DEV).to(dtype)
-    vc = torch.randn(N, H, D, 16, generator=g, device=DEV).to(dtype)
-    hk, hv = _pinned_like(NH, pa.k_cache_shape(NH, H, D)[1:], dtype), _pinned_like(NH, (H, D, 16), dtype)
+    vc = torch.randn(pa.v_cache_shape(N, H, D), generator=g, device=DEV).to(dtype)
+    hk, hv = _pinned_like(NH, pa.k_cache_shape(NH, H, D)[1:], dtype), _pinned_like(NH, pa.v_cache_shape(NH, H, D)[1:], dtype)
     want_dk, want_dv, want_hk, want_hv = bits(kc), bits(vc), bits(hk), bits(hv)
     out_pairs = np.array([[3, 0], [17, 8], [0, 4], [5, 11], [25, 1]], dtype=np.int32)   # last two skipped
     pa.swap_blocks(kc, vc, hk, hv, torch.from_numpy(out_pairs).to(DEV), pa.PA_SWAP_OUT)
@@ -57,8 +57,8 @@ def test_sequence_swapped_out_and_in_decodes_identically():
     pool = pa.BlockPool(N, 16, 21, num_host_blocks=NH)
     g = torch.Generator(device=DEV).manual_seed(21)
     kc = torch.full(pa.k_cache_shape(N, H, D), float("nan"), dtype=dtype, device=DEV)
-    vc = torch.full((N, H, D, 16), float("nan"), dtype=dtype, device=DEV)
-    hk, hv = _pinned_like(NH, pa.k_cache_shape(NH, H, D)[1:], dtype), _pinned_like(NH, (H, D, 16), dtype)
+    vc = torch.full(pa.v_cache_shape(N, H, D), float("nan"), dtype=dtype, device=DEV)
+    hk, hv = _pinned_like(NH, pa.k_cache_shape(NH, H, D)[1:], dtype), _pinned_like(NH, pa.v_cache_shape(NH, H, D)[1:], dtype)
 
     def grow(sid, n):
         slots, cow = pool.append(sid, n)

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 def _sentinel_cache(N, H, D, dtype):
     k = torch.full(pa.k_cache_shape(N, H, D), 0, dtype=torch.int16, device=DEV)
-    v = torch.full((N, H, D, 16), 0, dtype=torch.int16, device=DEV)
+    v = torch.full(pa.v_cache_shape(N, H, D), 0, dtype=torch.int16, device=DEV)
     k.fill_(-21555)   # 0xABCD pattern
     v.fill_(-21555)
     return k.view(dtype), v.view(dtype)
@@ -47,12 +47,13 @@ def test_write_kv_bit_exact(dtype, H, D):
 def test_write_kv_runs_and_scattered_tokens(dtype, H, D):
     """Token groups whose slots are whole aligned runs (prefill filling its
     blocks in order), runs that start mid-block or cross blocks, runs with a
-    skipped token inside, lone decode tokens, and a ragged last group."""
+    skipped token inside, lone decode tokens, runs aligned to four slots that
+    start mid-block, and a ragged last group."""
     print(f"write_kv runs dtype={dtype} H={H} D={D}", flush=True)
     N = 64
     rng = np.random.default_rng(9)
     blocks = rng.permutation(N - 4)      # blocks N-4 .. N-1 are kept for the crossing run
-    lone = iter(int(b) * 16 + int(rng.integers(16)) for b in blocks[20:56])
+    lone = iter(int(b) * 16 + int(rng.integers(16)) for b in blocks[20:60])
     run = lambda b, start, n: [int(b) * 16 + start + j for j in range(n)]
     groups = [
         run(blocks[0], 0, 16),                                  # whole block
@@ -63,6 +64,7 @@ def test_write_kv_runs_and_scattered_tokens(dtype, H, D):
         run(blocks[5], 3, 13) + [next(lone) for _ in range(3)], # starts mid-block
         run(N - 4, 5, 16),                                      # crosses into the next block
         [next(lone) for _ in range(16)],                        # decode-like
+        run(blocks[7], 4, 12) + [next(lone) for _ in range(4)], # 4-aligned runs from mid-block
     ]
     groups[4][4] = -1
     slots = [x for grp in groups for x in grp] + run(blocks[6], 0, 11)   # ragged last group
@@ -101,7 +103,7 @@ def test_copy_blocks_bit_exact(dtype):
     g = torch.Generator(device=DEV).manual_seed(2)
     N, H, D = 30, 8, 128
     kc = torch.randn(pa.k_cache_shape(N, H, D), generator=g, device=DEV).to(dtype)
-    vc = torch.randn(N, H, D, 16, generator=g, device=DEV).to(dtype)
+    vc = torch.randn(pa.v_cache_shape(N, H, D), generator=g, device=DEV).to(dtype)
     want_k, want_v = bits(kc), bits(vc)
     pairs = np.array([[1, 20], [3, 21], [29, 0], [7, 22], [2, 40]], dtype=np.int32)  # last: out of range
     pa.copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV))

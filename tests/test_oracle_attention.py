@@ -35,13 +35,18 @@ def kshape(N, Hkv, D):
     return (N, Hkv, D // 32, B, 32)
 
 
+def vshape(N, Hkv, D):
+    """V cache shape in the library's storage format: groups of four slots, dim-major within a group."""
+    return (N, Hkv, B // 4, D, 4)
+
+
 def paged_layout(rng, lens, Hkv, D, dtype, extra=3):
     """Random scattered cache holding per-sequence logical K/V."""
     nb = [-(-L // B) for L in lens]
     N = sum(nb) + extra
     perm = rng.permutation(N)
     kc = rand_bits(rng, kshape(N, Hkv, D), dtype)
-    vc = rand_bits(rng, (N, Hkv, D, B), dtype)
+    vc = rand_bits(rng, vshape(N, Hkv, D), dtype)
     bt = np.zeros((len(lens), max(max(nb), 1)), dtype=np.int32)
     at = 0
     for s, n in enumerate(nb):
@@ -86,7 +91,7 @@ def brute_decode(q, kc, vc, bt, lens, scale, dtype, Hkv):
         for h in range(Hq):
             g = h // G
             K = [[kf[bt[s][t // B], g, d // 32, t % B, d % 32] for d in range(D)] for t in range(lens[s])]
-            V = [[vf[bt[s][t // B], g, d, t % B] for d in range(D)] for t in range(lens[s])]
+            V = [[vf[bt[s][t // B], g, (t % B) // 4, d, t % 4] for d in range(D)] for t in range(lens[s])]
             out[s, h] = brute_attend(list(qf[s, h]), K, V, A.scale64(scale))
     return out
 
@@ -146,10 +151,11 @@ def test_tiny_workload_shape_brute_force():
 
 def _dense_from_identity(kc, vc, L, g, dtype):
     nb = -(-L // B)
-    D = vc.shape[2]
+    D = vc.shape[3]
     # K [nb, D/32, B, 32]: key (block j, slot t), dim 32c + e sits at [j, c, t, e]
     K = A.widen(np.ascontiguousarray(np.swapaxes(kc[:nb, g], 1, 2)), dtype).reshape(-1, D)[:L]
-    V = A.widen(np.swapaxes(vc[:nb, g], 1, 2), dtype).reshape(-1, D)[:L]
+    # V [nb, B/4, D, 4]: value (block j, slot 4u + r), dim d sits at [j, u, d, r]
+    V = A.widen(np.ascontiguousarray(np.swapaxes(vc[:nb, g], 2, 3)), dtype).reshape(-1, D)[:L]
     return K, V
 
 
@@ -159,7 +165,7 @@ def test_decode_identity_table_equals_sdpa(dtype):
     Hq, Hkv, D, L = 8, 2, 64, 77
     nb = -(-L // B)
     kc = rand_bits(rng, kshape(nb, Hkv, D), dtype)
-    vc = rand_bits(rng, (nb, Hkv, D, B), dtype)
+    vc = rand_bits(rng, vshape(nb, Hkv, D), dtype)
     q = rand_bits(rng, (1, Hq, D), dtype)
     bt = np.arange(nb, dtype=np.int32)[None]
     scale = 1.0 / math.sqrt(D)
@@ -181,7 +187,7 @@ def test_prefill_identity_table_equals_sdpa_with_causal_mask():
     L = n_cached + n
     nb = -(-L // B)
     kc = rand_bits(rng, kshape(nb, Hkv, D), dtype)
-    vc = rand_bits(rng, (nb, Hkv, D, B), dtype)
+    vc = rand_bits(rng, vshape(nb, Hkv, D), dtype)
     q = rand_bits(rng, (n, Hq, D), dtype)
     bt = np.arange(nb, dtype=np.int32)[None]
     scale = 1.0 / math.sqrt(D)
@@ -218,7 +224,7 @@ def test_single_key_returns_that_value_exactly():
         kc, vc, bt = paged_layout(rng, [1], 2, 32, dtype)
         q = rand_bits(rng, (1, 2, 32), dtype)
         o = A.decode(q, kc, vc, bt, [1], 0.3, dtype)
-        v0 = A.widen(vc[bt[0, 0], :, :, 0], dtype)
+        v0 = A.widen(vc[bt[0, 0], :, 0, :, 0], dtype)
         assert np.array_equal(o[0], v0)
 
 
@@ -313,7 +319,7 @@ def test_shared_prefix_reads_like_private_copies():
     # shared layout: full prefix blocks shared, partial last prefix block
     # copied for every sequence that writes past the prefix.
     N = 40
-    kc = np.zeros(kshape(N, Hkv, D), np.float16); vc = np.zeros((N, Hkv, D, B), np.float16)
+    kc = np.zeros(kshape(N, Hkv, D), np.float16); vc = np.zeros(vshape(N, Hkv, D), np.float16)
     shared = [0, 1]                           # holds tokens 0..31
     nxt = 2
     bt = np.zeros((3, 8), np.int32)
@@ -384,12 +390,12 @@ def _drops_last_key(q, K, V, scale, return_probs=False):
     return _good_attend(q, K, V, scale, return_probs)
 
 
-def _values_not_transposed(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype):
+def _values_read_slot_major(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype):
     K, _ = _good_gather(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype)
     nb = -(-n_tokens // block_size)
     phys = np.asarray(bt_row[:nb], dtype=np.int64)
-    raw = np.ascontiguousarray(v_cache[phys, kv_head])  # read [D, B] as if [B, D]
-    V = A.widen(raw, dtype).reshape(-1, v_cache.shape[2])[:n_tokens]
+    raw = np.ascontiguousarray(v_cache[phys, kv_head])  # read [B/4, D, 4] as if [B, D]
+    V = A.widen(raw, dtype).reshape(-1, v_cache.shape[3])[:n_tokens]
     return K, V
 
 
@@ -398,7 +404,7 @@ def _keys_read_slot_major(k_cache, v_cache, bt_row, n_tokens, kv_head, block_siz
     nb = -(-n_tokens // block_size)
     phys = np.asarray(bt_row[:nb], dtype=np.int64)
     raw = np.ascontiguousarray(k_cache[phys, kv_head])  # read [D/32, B, 32] as if [B, D]
-    K = A.widen(raw, dtype).reshape(-1, v_cache.shape[2])[:n_tokens]
+    K = A.widen(raw, dtype).reshape(-1, v_cache.shape[3])[:n_tokens]
     return K, V
 
 
@@ -423,7 +429,7 @@ def _wrong_slot(k_cache, v_cache, bt_row, n_tokens, kv_head, block_size, dtype):
     ("off-by-one context", "attend", _drops_last_key, lambda: test_decode_matches_brute_force(
         "bf16", dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=64))),
     ("off-by-one causal (prefill)", "attend", _drops_last_key, test_prefill_identity_table_equals_sdpa_with_causal_mask),
-    ("V storage read untransposed", "gather_kv", _values_not_transposed, test_shared_prefix_reads_like_private_copies),
+    ("V storage read slot-major", "gather_kv", _values_read_slot_major, test_shared_prefix_reads_like_private_copies),
     ("K chunks read as slot-major rows", "gather_kv", _keys_read_slot_major, lambda: test_decode_identity_table_equals_sdpa("fp16")),
     ("K chunks read as slot-major rows (brute force)", "gather_kv", _keys_read_slot_major, lambda: test_decode_matches_brute_force(
         "bf16", dict(lens=[5, 16, 32], Hq=4, Hkv=2, D=64))),

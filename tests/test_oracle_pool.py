@@ -91,19 +91,19 @@ def test_paged_waste_below_pages_bound_on_synthetic_lengths():
 def test_write_kv_places_tokens_and_skips_negative_slots():
     N, H, B, D = 6, 2, 16, 64
     kc = np.full((N, H, D // 32, B, 32), 0xFFFF, np.uint16)   # element d of slot s at [.., d // 32, s, d % 32]
-    vc = np.full((N, H, D, B), 0xFFFF, np.uint16)
+    vc = np.full((N, H, B // 4, D, 4), 0xFFFF, np.uint16)   # element d of slot s at [.., s // 4, d, s % 4]
     k = np.arange(3 * H * D, dtype=np.uint16).reshape(3, H, D)
     v = (1000 + np.arange(3 * H * D)).astype(np.uint16).reshape(3, H, D)
     KC.write_kv(kc, vc, k, v, [5 * 16 + 15, -1, 2 * 16 + 0], 16)
     for d in (0, 31, 32, 63):
         assert np.array_equal(kc[5, :, d // 32, 15, d % 32], k[0][:, d])
         assert np.array_equal(kc[2, :, d // 32, 0, d % 32], k[2][:, d])
-    assert np.array_equal(vc[5, :, :, 15], v[0]) and np.array_equal(vc[2, :, :, 0], v[2])
+    assert np.array_equal(vc[5, :, 3, :, 3], v[0]) and np.array_equal(vc[2, :, 0, :, 0], v[2])
     touched = np.zeros((N, B), bool); touched[5, 15] = touched[2, 0] = True
     for b in range(N):
         for o in range(B):
             if not touched[b, o]:
-                assert np.all(kc[b, :, :, o, :] == 0xFFFF) and np.all(vc[b, :, :, o] == 0xFFFF)
+                assert np.all(kc[b, :, :, o, :] == 0xFFFF) and np.all(vc[b, :, o // 4, :, o % 4] == 0xFFFF)
 
 
 def test_swap_blocks_round_trip_and_skips_bad_ids():

@@ -80,7 +80,7 @@ class DecodeWorkload:
     def cache_shapes(self):
         """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, D, B] (dim-major)."""
         N, H, B, D = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
-        return (N, H, D // 32, B, 32), (N, H, D, B)
+        return (N, H, D // 32, B, 32), (N, H, B // 4, D, 4)
 
     def make_tensors(self, device="cpu", seed_offset=0):
         """q [S, Hq, D], k_cache [N, Hkv, D/32, B, 32], v_cache [N, Hkv, D, B]."""
@@ -268,7 +268,7 @@ class MixedWorkload:
     def cache_shapes(self):
         """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, D, B] (dim-major)."""
         N, H, B, D = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
-        return (N, H, D // 32, B, 32), (N, H, D, B)
+        return (N, H, D // 32, B, 32), (N, H, B // 4, D, 4)
 
     def make_tensors(self, device="cpu"):
         """Pre-step caches, new k/v [T, Hkv, D], decode q [S_dec, Hq, D],
