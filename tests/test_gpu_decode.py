@@ -146,20 +146,22 @@ def test_batch_invariance_is_bit_exact():
 # two-pass kernels (partition states through the workspace).  Both must give
 # the same bits.  Cases: bf16 GQA at the 8B workload's 512-token partitions
 # (4-wave groups), fp16 MHA at 256-token partitions, bf16 GQA at 2048-token
-# partitions (8-wave groups).
-@pytest.mark.parametrize("dtype,S,Hq,Hkv,P,max_len", [
-    (torch.bfloat16, 128, 32, 8, 512, 4096),
-    (torch.float16, 32, 32, 32, 256, 2048),
-    (torch.bfloat16, 128, 32, 8, 2048, 4096),
-], ids=["bf16-gqa-P512", "fp16-mha-P256", "bf16-gqa-P2048"])
-def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, P, max_len):
+# partitions (8-wave groups), head_dim 64 with 8- and 2-head groups.
+@pytest.mark.parametrize("dtype,S,Hq,Hkv,D,P,max_len", [
+    (torch.bfloat16, 128, 32, 8, 128, 512, 4096),
+    (torch.float16, 32, 32, 32, 128, 256, 2048),
+    (torch.bfloat16, 128, 32, 8, 128, 2048, 4096),
+    (torch.float16, 128, 64, 8, 64, 1024, 4096),
+    (torch.bfloat16, 64, 32, 16, 64, 256, 1024),
+], ids=["bf16-gqa4-P512", "fp16-mha-P256", "bf16-gqa4-P2048", "fp16-gqa8-D64-P1024", "bf16-gqa2-D64-P256"])
+def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_len):
     rng = np.random.default_rng(21)
     lens = rng.integers(1, max_len + 1, S)
     # edges: one block, a partition exactly, one key past it, the maximum,
     # and an odd number of partitions
     lens[:6] = [1, 16, P, P + 1, max_len, min(3 * P - 5, max_len - 3)]
-    q, kc, vc, bt, ctx = small_case(S, Hq, Hkv, 128, dtype, lens, seed=22, extra_blocks=8)
-    print(f"single pass: S={S} Hq={Hq} Hkv={Hkv} P={P} blocks={kc.shape[0]}", flush=True)
+    q, kc, vc, bt, ctx = small_case(S, Hq, Hkv, D, dtype, lens, seed=22, extra_blocks=8)
+    print(f"single pass: S={S} Hq={Hq} Hkv={Hkv} D={D} P={P} blocks={kc.shape[0]}", flush=True)
     full = run_decode(q, kc, vc, bt, ctx, max_len, 0.088, P)
     for s in range(8):
         one = run_decode(q[s:s + 1].contiguous(), kc, vc, bt[s:s + 1], ctx[s:s + 1], max_len, 0.088, P)
