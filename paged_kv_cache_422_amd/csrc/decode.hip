@@ -20,8 +20,11 @@
 // w takes blocks w, w+4, ... of the partition; waves merge through LDS.  A
 // sequence with one partition writes its output directly; otherwise each
 // partition writes (max, sum, unnormalised accumulator) and a second kernel
-// merges them by log-sum-exp.  The order of every reduction depends only on
-// the sequence's own length and the partition size, so the result for a
+// merges them by log-sum-exp.  When the batch alone fills the GPU, one
+// workgroup instead takes all partitions of a sequence and merges them in
+// LDS with the same arithmetic (decode_fused_kernel), so partition states
+// never go through HBM.  The order of every reduction depends only on the
+// sequence's own length and the partition size, so the result for a
 // sequence does not depend on the rest of the batch or on where its blocks
 // live.
 //
@@ -431,7 +434,7 @@ void decode_fused_kernel(DecodeArgs a) {
   __shared__ float sm_o[PMAX][W][NH][D];
   __shared__ float sm_ml[NH][PMAX][2];
 
-  // blockIdx.x = s * num_kv_heads + KV head (one head sub-group: group <= 16)
+  // blockIdx.x = s * num_kv_heads + KV head (one head sub-group: the host sends group <= 8)
   const int g = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.num_kv_heads));
   const int s = static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.num_kv_heads));
   const int hq0 = g * a.group;
