@@ -173,6 +173,23 @@ int32_t   pa_default_partition_size(int32_t num_seqs, int32_t num_q_heads, int32
 pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t partition_size,
                                    int32_t num_kv_heads, size_t* bytes);
+/* How pa_decode would run for these sizes, without launching anything:
+ *   partition_out  the partition size it uses (partition_size, or the library
+ *                  default when 0), in tokens;
+ *   merge_out      PA_MERGE_NONE (one partition per sequence),
+ *                  PA_MERGE_ON_CHIP (partition states merged in LDS, one
+ *                  kernel) or PA_MERGE_TWO_PASS (partition kernel, then the
+ *                  log-sum-exp merge kernel through the workspace);
+ *   waves_out      waves that interleave the blocks of one partition (4 or 8).
+ * The choice never changes results (both merges give the same bits); it is
+ * reported for callers that size work or check which kernels run.  Any output
+ * pointer may be NULL.  Errors as pa_decode's size checks. */
+#define PA_MERGE_NONE 0
+#define PA_MERGE_ON_CHIP 1
+#define PA_MERGE_TWO_PASS 2
+pa_status pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                         int32_t* partition_out, int32_t* merge_out, int32_t* waves_out);
 pa_status pa_decode(void* out, const void* q,
                     const void* k_cache, const void* v_cache, int64_t num_blocks,
                     const int32_t* block_tables, int32_t bt_stride,

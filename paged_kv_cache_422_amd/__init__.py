@@ -51,6 +51,7 @@ _SIGS = {
     "pa_default_partition_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_workspace_size": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          ctypes.POINTER(c_sz)]),
+    "pa_decode_plan": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, P_i32, P_i32, P_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_i32, c_vp]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32,
@@ -195,6 +196,18 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
     _check(_lib.pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                          partition_size, num_kv_heads, ctypes.byref(out)))
     return int(out.value)
+
+
+MERGE_NONE, MERGE_ON_CHIP, MERGE_TWO_PASS = 0, 1, 2
+
+
+def decode_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size=0):
+    """(partition size, merge kind, waves per partition) that decode would use."""
+    part, merge, waves = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_lib.pa_decode_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                               partition_size, ctypes.byref(part), ctypes.byref(merge),
+                               ctypes.byref(waves)))
+    return int(part.value), int(merge.value), int(waves.value)
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,

@@ -240,6 +240,64 @@ pa_status pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The partitioning fields of a decode call (partition size resolved, waves,
+// single pass or two), shared by pa_decode and pa_decode_plan so that the
+// plan reported is the one launched.
+void fill_decode_plan(pa::DecodeArgs& a, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t P, int32_t max_context_len) {
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t num_sub = (group + 15) / 16;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_sub = num_sub;
+  a.part_blocks = P / kBlock;
+  a.max_parts = static_cast<int32_t>(std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P));
+  a.max_context_len = max_context_len;
+  a.waves = decode_waves(a.part_blocks);
+  a.fuse_groups = decode_fuse_groups(static_cast<int64_t>(num_seqs) * num_kv_heads * num_sub, group,
+                                     max_context_len);
+}
+
+pa_status check_decode_shape(const char* fn, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+  if (pa_status st = check_common(fn, num_kv_heads, head_dim, kBlock, PA_FP16)) return st;
+  if (num_seqs < 0 || max_context_len < 0)
+    return fail(PA_EINVAL, std::string(fn) + ": negative size");
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, std::string(fn) + ": num_q_heads must be a positive multiple of num_kv_heads");
+  if (partition_size != 0 &&
+      (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > kMaxPartitionTokens))
+    return fail(PA_ENOTSUP, std::string(fn) + ": partition_size must be 0 or a multiple of 16 in [16, 4096]");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t partition_size, int32_t* partition_out,
+                         int32_t* merge_out, int32_t* waves_out) {
+  const char* fn = "pa_decode_plan";
+  if (pa_status st = check_decode_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                        partition_size))
+    return st;
+  const int32_t P = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      max_context_len);
+  pa::DecodeArgs a{};
+  fill_decode_plan(a, num_seqs, num_q_heads, num_kv_heads, P, max_context_len);
+  if (partition_out) *partition_out = P;
+  if (merge_out) *merge_out = pa::decode_merge_kind(a, head_dim);
+  if (waves_out) *waves_out = a.waves;
+  return ok();
+}
+
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -292,17 +350,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.context_lens = context_lens;
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = group;
-  a.num_sub = num_sub;
-  a.part_blocks = P / kBlock;
-  a.max_parts = static_cast<int32_t>(max_parts);
-  a.max_context_len = max_context_len;
-  a.waves = decode_waves(a.part_blocks);
-  a.fuse_groups = decode_fuse_groups(static_cast<int64_t>(num_seqs) * num_kv_heads * num_sub, group,
-                                     max_context_len);
+  fill_decode_plan(a, num_seqs, num_q_heads, num_kv_heads, P, max_context_len);
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_result(fn, pa::launch_decode(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
 }

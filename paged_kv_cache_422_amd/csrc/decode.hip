@@ -651,32 +651,44 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
                          a.out + row * D);
 }
 
-template <class T, int D, int NH, int W, int NGRP>
-bool launch_fused(const DecodeArgs& a, hipStream_t stream) {
-  if (a.max_parts > fused_max_parts<W, NH, D, NGRP>()) return false;
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_kv_heads));
-  hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, W, NGRP>), grid, dim3(64 * W * NGRP), 0, stream, a);
-  return true;
+// How one call merges partitions, for query-head groups of NH (template
+// bucket) and head_dim D: kMergeOnChip when the host chose the single pass
+// (fuse_groups > 0: the batch fills the GPU without splitting, a sequence's
+// table fits the registers and a head group is at most 8 query heads) and the
+// partitions fit the kernel's LDS; kMergeTwoPass otherwise.
+template <int D, int NH>
+int merge_kind_nh(const DecodeArgs& a) {
+  if (a.max_parts <= 1) return kMergeNone;
+  if constexpr (NH > 8) {
+    return kMergeTwoPass;
+  } else {
+    if (a.fuse_groups <= 0 || a.num_sub != 1) return kMergeTwoPass;
+    const int cap = a.waves == 8            ? fused_max_parts<8, NH, D, 1>()
+                    : a.fuse_groups == 2    ? fused_max_parts<4, NH, D, 2>()
+                                            : fused_max_parts<4, NH, D, 1>();
+    return a.max_parts <= cap ? kMergeOnChip : kMergeTwoPass;
+  }
 }
 
-// The single-pass kernel, when the host chose it (fuse_groups > 0: the batch
-// fills the GPU without splitting, a sequence's table fits the registers and
-// a head group is at most 8 query heads) and the partitions fit its LDS.
-template <class T, int D, int NH>
-bool try_fused(const DecodeArgs& a, hipStream_t stream) {
-  if constexpr (NH > 8) {
-    return false;
-  } else {
-    if (a.fuse_groups <= 0 || a.max_parts <= 1 || a.num_sub != 1) return false;
-    if (a.waves == 8) return launch_fused<T, D, NH, 8, 1>(a, stream);
-    if (a.fuse_groups == 2) return launch_fused<T, D, NH, 4, 2>(a, stream);
-    return launch_fused<T, D, NH, 4, 1>(a, stream);
-  }
+template <class T, int D, int NH, int W, int NGRP>
+void launch_fused(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_kv_heads));
+  hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, W, NGRP>), grid, dim3(64 * W * NGRP), 0, stream, a);
 }
 
 template <class T, int D, int NH>
 hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
-  if (try_fused<T, D, NH>(a, stream)) return hipGetLastError();
+  if constexpr (NH <= 8) {
+    if (merge_kind_nh<D, NH>(a) == kMergeOnChip) {
+      if (a.waves == 8)
+        launch_fused<T, D, NH, 8, 1>(a, stream);
+      else if (a.fuse_groups == 2)
+        launch_fused<T, D, NH, 4, 2>(a, stream);
+      else
+        launch_fused<T, D, NH, 4, 1>(a, stream);
+      return hipGetLastError();
+    }
+  }
   const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
   const dim3 grid(static_cast<uint32_t>(n_wg));
   if (a.waves == 8)
@@ -691,17 +703,39 @@ hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Query heads per work item, rounded up to the template bucket 1, 2, 4, 8, 16.
+int nh_bucket(int group) {
+  const int nh = group < 16 ? group : 16;
+  return nh <= 1 ? 1 : nh <= 2 ? 2 : nh <= 4 ? 4 : nh <= 8 ? 8 : 16;
+}
+
 template <class T, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  const int nh = a.group < 16 ? a.group : 16;
-  if (nh <= 1) return launch_nh<T, D, 1>(a, stream);
-  if (nh <= 2) return launch_nh<T, D, 2>(a, stream);
-  if (nh <= 4) return launch_nh<T, D, 4>(a, stream);
-  if (nh <= 8) return launch_nh<T, D, 8>(a, stream);
-  return launch_nh<T, D, 16>(a, stream);
+  switch (nh_bucket(a.group)) {
+    case 1: return launch_nh<T, D, 1>(a, stream);
+    case 2: return launch_nh<T, D, 2>(a, stream);
+    case 4: return launch_nh<T, D, 4>(a, stream);
+    case 8: return launch_nh<T, D, 8>(a, stream);
+    default: return launch_nh<T, D, 16>(a, stream);
+  }
+}
+
+template <int D>
+int merge_kind_d(const DecodeArgs& a) {
+  switch (nh_bucket(a.group)) {
+    case 1: return merge_kind_nh<D, 1>(a);
+    case 2: return merge_kind_nh<D, 2>(a);
+    case 4: return merge_kind_nh<D, 4>(a);
+    case 8: return merge_kind_nh<D, 8>(a);
+    default: return merge_kind_nh<D, 16>(a);
+  }
 }
 
 }  // namespace
+
+int decode_merge_kind(const DecodeArgs& a, int head_dim) {
+  return head_dim == 64 ? merge_kind_d<64>(a) : merge_kind_d<128>(a);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int dtype, hipStream_t stream) {
   if (dtype == 0) return head_dim == 64 ? launch_d<F16, 64>(a, stream) : launch_d<F16, 128>(a, stream);

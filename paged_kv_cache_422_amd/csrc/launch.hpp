@@ -82,6 +82,9 @@ struct PrefillArgs {
 hipError_t launch_write_kv(const WriteKvArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int dtype, hipStream_t stream);
+// How launch_decode merges a call's partitions (also reported by pa_decode_plan).
+enum { kMergeNone = 0, kMergeOnChip = 1, kMergeTwoPass = 2 };
+int decode_merge_kind(const DecodeArgs& a, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStream_t stream);
 
 }  // namespace pa

@@ -35,6 +35,34 @@ def test_version():
     assert "gfx950" in pa.version()
 
 
+def test_decode_plan_reports_the_merge_path():
+    """The single pass is chosen exactly when the batch alone fills the GPU
+    (>= 1024 sequence-KV-head items), a head group has at most 8 query heads,
+    contexts fit 4096 tokens and the partitions fit the kernel's LDS; a call
+    with one partition per sequence needs no merge at all."""
+    # (num_seqs, Hq, Hkv, D, max_ctx, P) -> (partition, merge, waves)
+    cases = [
+        ((256, 32, 8, 128, 4096, 512), (512, pa.MERGE_ON_CHIP, 4)),     # 8B GQA workload
+        ((1, 32, 8, 128, 4096, 512), (512, pa.MERGE_TWO_PASS, 4)),      # same sizes, one sequence
+        ((127, 32, 8, 128, 4096, 512), (512, pa.MERGE_TWO_PASS, 4)),    # 1016 items: below the threshold
+        ((128, 32, 8, 128, 4096, 2048), (2048, pa.MERGE_ON_CHIP, 8)),   # long partitions: 8 waves
+        ((64, 32, 32, 128, 2048, 2048), (2048, pa.MERGE_NONE, 8)),      # 7B workload: no split
+        ((128, 64, 8, 64, 4096, 1024), (1024, pa.MERGE_ON_CHIP, 4)),    # 8-head groups, head_dim 64
+        ((128, 128, 8, 128, 4096, 512), (512, pa.MERGE_TWO_PASS, 4)),   # 16-head groups: two passes
+        ((1024, 8, 8, 128, 8192, 4096), (4096, pa.MERGE_TWO_PASS, 8)),  # contexts beyond 4096 tokens
+        ((256, 32, 8, 128, 4096, 16), (16, pa.MERGE_TWO_PASS, 4)),      # 256 partitions: beyond LDS
+    ]
+    for args, want in cases:
+        assert pa.decode_plan(*args) == want, args
+    P = pa.default_partition_size(4, 32, 8, 128, 4096)
+    assert pa.decode_plan(4, 32, 8, 128, 4096) == (P, pa.MERGE_TWO_PASS, 4 if P < 2048 else 8)
+    for bad, code in (((4, 33, 8, 128, 4096, 0), pa.PA_EINVAL), ((4, 32, 8, 96, 4096, 0), pa.PA_ENOTSUP),
+                      ((4, 32, 8, 128, 4096, 40), pa.PA_ENOTSUP), ((-1, 32, 8, 128, 4096, 0), pa.PA_EINVAL)):
+        with pytest.raises(pa.PAError) as e:
+            pa.decode_plan(*bad)
+        assert e.value.status == code
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=96), pa.PA_ENOTSUP),
     (dict(block_size=32), pa.PA_ENOTSUP),

@@ -162,6 +162,8 @@ def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_le
     lens[:6] = [1, 16, P, P + 1, max_len, min(3 * P - 5, max_len - 3)]
     q, kc, vc, bt, ctx = small_case(S, Hq, Hkv, D, dtype, lens, seed=22, extra_blocks=8)
     print(f"single pass: S={S} Hq={Hq} Hkv={Hkv} D={D} P={P} blocks={kc.shape[0]}", flush=True)
+    assert pa.decode_plan(S, Hq, Hkv, D, max_len, P)[1] == pa.MERGE_ON_CHIP
+    assert pa.decode_plan(1, Hq, Hkv, D, max_len, P)[1] == pa.MERGE_TWO_PASS
     full = run_decode(q, kc, vc, bt, ctx, max_len, 0.088, P)
     for s in range(8):
         one = run_decode(q[s:s + 1].contiguous(), kc, vc, bt[s:s + 1], ctx[s:s + 1], max_len, 0.088, P)
