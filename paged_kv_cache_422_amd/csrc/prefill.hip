@@ -212,7 +212,7 @@ void prefill_kernel(PrefillArgs a) {
       const int lb = t * kTileBlocks + (r * kPrefillThreads + w * 64) / UPB;
       const int wu = u % UPB;
       // Blocks past the sequence end read its last block (always valid); the
-      // stash zeroes them.
+      // stash zeroes their V, and their keys are masked.
       int id = bt[min(lb, nb_seq - 1)];
       if (id < 0 || id >= a.num_blocks) {
         bad_id |= lb < nb_seq;
@@ -238,11 +238,13 @@ void prefill_kernel(PrefillArgs a) {
       const int wu = u % UPB;
       // K unit wu is 16 bytes of 32-dim chunk wu / 64: key (wu / 4) % 16,
       // dims 32 * (wu / 64) + 8 * (wu % 4) .. +7.
+      // Keys past the sequence end are stored as read (the last block's
+      // stale slots, or the last block again): every tile that reaches past a
+      // row's last visible key replaces those scores by -inf with a select,
+      // so whatever they hold, NaN included, never reaches the softmax.
       const int kt = b * kBlock + ((wu >> 2) & (kBlock - 1));   // key within the tile
       const int row = (kt & 32) | swap_bits23(kt & 31);
-      const bool live = t * kTileBlocks + b < nb_seq;
-      *reinterpret_cast<u32x4*>(lds + row * Lds::kRow + ((wu >> 6) * 4 + (wu & 3)) * 16) =
-          live ? pk[r] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(lds + row * Lds::kRow + ((wu >> 6) * 4 + (wu & 3)) * 16) = pk[r];
       // V unit wu is 16 bytes of key group kg = wu / (D/2): dims d0 and
       // d0 + 1 (d0 = 2 * (wu % (D/2))), keys 4*kg .. +3 of each; dword e holds
       // dim d0 + e/2, keys 4*kg + 2*(e%2) and the next.
