@@ -250,11 +250,11 @@ void prefill_kernel(PrefillArgs a) {
       // dim d0 + e/2, keys 4*kg + 2*(e%2) and the next.
       const int kg = wu / (D / 2);
       const int d0 = 2 * (wu % (D / 2));
+      // Keys of this group past the sequence end (all four when n_ok <= 0)
+      // are zeroed half by half.
       u32x4 v = pv[r];
       const int n_ok = L - ((t * kTileBlocks + b) * kBlock + 4 * kg);   // keys of this group in range
-      if (n_ok <= 0) {
-        v = u32x4{0, 0, 0, 0};
-      } else if (n_ok < 4) {
+      if (n_ok < 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = 2 * (e & 1);
