@@ -195,6 +195,9 @@ void prefill_kernel(PrefillArgs a) {
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
   const int64_t head_off = static_cast<int64_t>(g) * tile_elems;
+  // Block ids are int32, so the pool bound can be too: the id check below
+  // then stays a 32-bit scalar compare (there is no 64-bit scalar compare).
+  const uint32_t nb_bound = static_cast<uint32_t>(min<int64_t>(a.num_blocks, INT32_MAX));
 
   // Cooperative loads of one key tile: unit u = r * threads + tid of each
   // tensor is 16 bytes of block u / UPB of the tile.  Two register sets hold
@@ -214,7 +217,7 @@ void prefill_kernel(PrefillArgs a) {
       // Blocks past the sequence end read its last block (always valid); the
       // stash zeroes their V, and their keys are masked.
       int id = bt[min(lb, nb_seq - 1)];
-      if (id < 0 || id >= a.num_blocks) {
+      if (static_cast<uint32_t>(id) >= nb_bound) {   // negative ids wrap to large
         bad_id |= lb < nb_seq;
         id = 0;
       }
@@ -248,7 +251,12 @@ void prefill_kernel(PrefillArgs a) {
       // V unit wu is 16 bytes of key group kg = wu / (D/2): dims d0 and
       // d0 + 1 (d0 = 2 * (wu % (D/2))), keys 4*kg .. +3 of each; dword e holds
       // dim d0 + e/2, keys 4*kg + 2*(e%2) and the next.
-      const int kg = wu / (D / 2);
+      // A wave's 64 units start at a multiple of 64; with D/2 = 64 units per
+      // key group (D = 128) they lie in one group, so kg is wave-uniform and
+      // the end-of-sequence test below is a scalar branch.  With D = 64 a
+      // wave covers two groups.
+      int kg = wu / (D / 2);
+      if constexpr ((D / 2) % 64 == 0) kg = __builtin_amdgcn_readfirstlane(kg);
       const int d0 = 2 * (wu % (D / 2));
       // Keys of this group past the sequence end (all four when n_ok <= 0)
       // are zeroed half by half.
