@@ -1,9 +1,9 @@
 """The mixed step (slot-mapped write, prefill chunks, split-KV decode with
-its merge pass) captured into a HIP graph: every replay, with the program's
-own eager work and synchronisations in between, reproduces the eager step
-bit for bit.  All three calls enqueue on the caller's stream, take their
-workspace from the caller and never allocate or set memory, so they can be
-captured."""
+its partitions merged by a second kernel, or on chip in one pass) captured
+into a HIP graph: every replay, with the program's own eager work and
+synchronisations in between, reproduces the eager step bit for bit.  All
+three calls enqueue on the caller's stream, take their workspace from the
+caller and never allocate or set memory, so they can be captured."""
 import pytest
 import torch
 
@@ -14,8 +14,13 @@ from tests.gpu_util import DEV
 pytestmark = pytest.mark.gpu
 
 
-def test_mixed_step_graph_replays_match_eager():
-    print("graph capture of the mixed step", flush=True)
+# Contexts up to 900 tokens: 32-token partitions (29 of them) are more than
+# the single pass's LDS holds, so the merge pass runs; 128-token partitions
+# (8) are merged on chip.
+@pytest.mark.parametrize("P,merge", [(32, pa.MERGE_TWO_PASS), (128, pa.MERGE_ON_CHIP)],
+                         ids=["two-pass", "on-chip"])
+def test_mixed_step_graph_replays_match_eager(P, merge):
+    print(f"graph capture of the mixed step, partitions of {P}", flush=True)
     w = W.mixed(num_decode=192, chunk=160, cached=96, lmin=16, lmax=900)
     kc0, vc0, k_new, v_new, q_dec, q_pre = w.make_tensors(DEV)
     sm = torch.from_numpy(w.slot_mapping).to(DEV)
@@ -24,7 +29,7 @@ def test_mixed_step_graph_replays_match_eager():
     psl = torch.from_numpy(w.prefill_seq_lens).to(DEV)
     dbt = torch.from_numpy(w.decode_bt).to(DEV)
     dctx = torch.from_numpy(w.decode_lens).to(DEV)
-    P = 128                                              # several partitions: the merge pass runs too
+    assert pa.decode_plan(w.num_decode, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_model_len, P)[1] == merge
     ws = torch.empty(pa.decode_workspace_size(w.num_decode, w.num_q_heads, w.head_dim, w.max_model_len, P,
                                               w.num_kv_heads), dtype=torch.uint8, device=DEV)
     assert ws.numel() > 0
