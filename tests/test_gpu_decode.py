@@ -159,7 +159,7 @@ def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_le
     lens = rng.integers(1, max_len + 1, S)
     # edges: one block, a partition exactly, one key past it, the maximum,
     # and an odd number of partitions
-    lens[:6] = [1, 16, P, P + 1, max_len, min(3 * P - 5, max_len - 3)]
+    lens[:7] = [1, 16, P, P + 1, max_len, min(3 * P - 5, max_len - 3), 0]
     q, kc, vc, bt, ctx = small_case(S, Hq, Hkv, D, dtype, lens, seed=22, extra_blocks=8)
     print(f"single pass: S={S} Hq={Hq} Hkv={Hkv} D={D} P={P} blocks={kc.shape[0]}", flush=True)
     assert pa.decode_plan(S, Hq, Hkv, D, max_len, P)[1] == pa.MERGE_ON_CHIP
@@ -171,13 +171,18 @@ def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_le
     seqs = list(range(8)) + [int(x) for x in rng.choice(np.arange(8, S), 8, replace=False)]
     want = oracle_decode(q, kc, vc, bt, ctx, 0.088, seqs=seqs)
     assert_close(full[seqs], want[seqs], what="single pass vs oracle")
-    # an out-of-range block id poisons only its own sequence's rows
+    f = full.float().cpu().numpy()
+    assert np.all(f[6] == 0)                              # empty context: zero rows
+    # an out-of-range block id, or a length beyond max_context_len, poisons
+    # only its own sequence's rows
     bt2 = bt.copy()
     bt2[3, 0] = kc.shape[0] + 7
-    bad = run_decode(q, kc, vc, bt2, ctx, max_len, 0.088, P).float().cpu().numpy()
-    assert np.all(np.isnan(bad[3]))
-    keep = [s for s in range(S) if s != 3]
-    assert np.array_equal(bad[keep], full.float().cpu().numpy()[keep])
+    ctx2 = ctx.copy()
+    ctx2[7] = max_len + 16
+    bad = run_decode(q, kc, vc, bt2, ctx2, max_len, 0.088, P).float().cpu().numpy()
+    assert np.all(np.isnan(bad[3])) and np.all(np.isnan(bad[7]))
+    keep = [s for s in range(S) if s not in (3, 7)]
+    assert np.array_equal(bad[keep], f[keep])
 
 
 def test_partition_size_changes_only_rounding():
