@@ -162,11 +162,12 @@ __device__ __forceinline__ void process_block(BlockRegs<T, D>& cur, int n_valid,
   }
 }
 
-// The W wave states of one partition merged for head h, dimension d: the
-// partition's max M, sum and unnormalised accumulator element.
+// The W (virtual) wave states of one partition merged for head h, dimension
+// d, in index order: the partition's max M, sum and unnormalised accumulator
+// element.
 template <int W, int NH, int D>
-__device__ __forceinline__ void merge_waves(const float (&sm_m)[W][NH], const float (&sm_l)[W][NH],
-                                            const float (&sm_o)[W][NH][D], int h, int d, float& M,
+__device__ __forceinline__ void merge_waves(const float (*sm_m)[NH], const float (*sm_l)[NH],
+                                            const float (*sm_o)[NH][D], int h, int d, float& M,
                                             float& lsum, float& acc) {
   M = -INFINITY;
 #pragma unroll
@@ -235,39 +236,242 @@ __device__ __forceinline__ void merge_partitions(const float* ml, const float* a
   for (int i = 0; i < PER; ++i) out_row[lane + 64 * i] = from_f32<T>(o[i] / lsum);
 }
 
-// W waves share one partition (W = 4 or 8); each keeps two blocks in flight
-// in three register buffers, which fits two waves per SIMD.
-template <class T, int D, int NH, int W>
+// Per-wave softmax states of NS segments (a segment is one virtual wave of
+// one partition): running max (log2 units), running sum and unnormalised
+// accumulator, for each of NH query heads.
+template <int NH, int D, int NS>
+struct WaveStates {
+  float m[NS][NH];
+  float l[NS][NH];
+  float o[NS][NH][D];
+};
+
+// The blocks of a partition are interleaved over VW virtual waves: virtual
+// wave v takes blocks start + v, start + v + VW, ... and keeps its own
+// softmax state, and the partition's state is the merge of its VW virtual
+// states in index order (merge_waves).  VW depends only on the partition
+// size, so it fixes the reduction order.  A workgroup runs a partition on pw
+// physical waves: physical wave wl runs virtual waves wl, wl + pw, ... one
+// after another, its register pipeline running on across the switch.  How
+// many physical waves a partition gets is therefore a free choice that
+// never changes a bit of the result.
+//
+// A cursor is a position in the list of (partition p, virtual wave v,
+// absolute block j) a physical wave visits: partitions p_first, p_first +
+// p_step, ... below p_end (partition p holds blocks [pstart(p), pstart(p +
+// 1))), virtual waves wl, wl + pw, ... below VW, blocks in steps of VW.  Its
+// state goes to segment slot p * VW + v.  p >= p_end once the wave is done.
+struct Cursor {
+  int p, v, j;
+};
+
+template <int VW, class PStart>
+struct SegmentWalk {
+  int p_step, p_end, wl, pw;
+  PStart pstart;
+
+  // Moves c to the first segment at or after (c.p, c.v) that holds a block.
+  __device__ __forceinline__ void enter(Cursor& c) const {
+    while (c.p < p_end) {
+      const int s0 = pstart(c.p);
+      if (c.v < VW && c.v < pstart(c.p + 1) - s0) {
+        c.j = s0 + c.v;
+        return;
+      }
+      c.p += p_step;
+      c.v = wl;
+    }
+  }
+  __device__ __forceinline__ Cursor first(int p_first) const {
+    Cursor c{p_first, wl, 0};
+    enter(c);
+    return c;
+  }
+  __device__ __forceinline__ void advance(Cursor& c) const {
+    if (c.p >= p_end) return;
+    c.j += VW;
+    if (c.j < pstart(c.p + 1)) return;
+    c.v += pw;
+    enter(c);
+  }
+};
+
+// Block ids of the blocks [b0, b0 + nb) of one table row, 64 per register
+// with one per lane (nb <= 64 * kBtRegs).  An id outside the pool reads
+// block 0 instead and is reported in `bad`.
+__device__ __forceinline__ void load_table(int (&bt)[kBtRegs], const int32_t* row, int nb, int lane,
+                                           int64_t num_blocks, bool& bad) {
+  bad = false;
+#pragma unroll
+  for (int r = 0; r < kBtRegs; ++r) {
+    bt[r] = 0;
+    if (64 * r < nb) {                        // wave-uniform
+      const int jj = 64 * r + lane;
+      if (jj < nb) bt[r] = row[jj];
+      const bool b = jj < nb && (bt[r] < 0 || bt[r] >= num_blocks);
+      bad |= b;
+      if (b) bt[r] = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ int64_t table_entry(const int (&bt)[kBtRegs], int jj) {
+  const int r = jj >> 6;                      // wave-uniform
+  int id = __builtin_amdgcn_readlane(bt[0], jj & 63);
+#pragma unroll
+  for (int k = 1; k < kBtRegs; ++k)
+    if (r == k) id = __builtin_amdgcn_readlane(bt[k], jj & 63);
+  return id;
+}
+
+// Everything one physical wave does for one (sequence, head group): walk its
+// segments with a three-buffer register pipeline (the loads of the next two
+// blocks are in flight while it works on the current one) and leave the
+// state of every segment it visits in st.  Segments it has no block in must
+// hold the empty state beforehand (store_empty).  `tbl_base` is the absolute
+// block index of table register lane 0.
+template <class T, int D, int NH, int NS, int VW, class Walk>
+__device__ __forceinline__ void run_wave(const Walk& walk, int p_first, const int (&bt)[kBtRegs], int tbl_base,
+                                         int L, const u32x4 (&qb)[D / 32], float scale_log2,
+                                         const uint16_t* kbase, const uint16_t* vbase, int64_t blk_elems,
+                                         int lane, WaveStates<NH, D, NS>& st) {
+  constexpr int VT = D / 16;
+  const int hl = lane & 15;
+  const int quad = lane >> 4;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 o[VT];
+#pragma unroll
+  for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int slot = -1;
+  auto flush = [&]() {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (lane < NH) {
+      st.m[slot][lane] = m_run;
+      st.l[slot][lane] = l_run;
+    }
+#pragma unroll
+    for (int t = 0; t < VT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = 4 * quad + e;
+        if (h < NH) st.o[slot][h][16 * t + hl] = o[t][e];
+      }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto process = [&](BlockRegs<T, D>& cur, const Cursor& c) __attribute__((always_inline)) {
+    const int sl = c.p * VW + c.v;
+    if (sl != slot) {
+      if (slot >= 0) flush();
+      slot = sl;
+    }
+    process_block<T, D>(cur, L - c.j * kBlock, qb, scale_log2, quad, m_run, l_run, o);
+  };
+  auto off = [&](int j) { return table_entry(bt, j - tbl_base) * blk_elems; };
+  // Past the end, prefetches read block 0 of the pool (the host rejects an
+  // empty pool when there is work): every wave's out-of-range prefetches
+  // share those lines, which then stay in L2, where re-reading a wave's own
+  // last block would go back to HBM under the non-temporal hint.  Issuing
+  // them unconditionally keeps the wait before each block to its own loads.
+  auto pf_off = [&](const Cursor& c) -> int64_t { return c.p < walk.p_end ? off(c.j) : int64_t(0); };
+
+  Cursor c0 = walk.first(p_first);
+  if (c0.p >= walk.p_end) return;
+  Cursor c1 = c0;
+  walk.advance(c1);
+  Cursor c2 = c1;
+  walk.advance(c2);
+  BlockRegs<T, D> b0, b1, b2;
+  load_block<T, D>(b0, kbase, vbase, off(c0.j));
+  load_block<T, D>(b1, kbase, vbase, pf_off(c1));
+  auto shift = [&]() {
+    c0 = c1;
+    c1 = c2;
+    walk.advance(c2);
+  };
+  for (;;) {
+    load_block<T, D>(b2, kbase, vbase, pf_off(c2));
+    process(b0, c0);
+    shift();
+    if (c0.p >= walk.p_end) break;
+    load_block<T, D>(b0, kbase, vbase, pf_off(c2));
+    process(b1, c0);
+    shift();
+    if (c0.p >= walk.p_end) break;
+    load_block<T, D>(b1, kbase, vbase, pf_off(c2));
+    process(b2, c0);
+    shift();
+    if (c0.p >= walk.p_end) break;
+  }
+  flush();
+}
+
+// The empty state (max -inf, sum 0, accumulator 0) in segment slot sl, as
+// left by a virtual wave with no block: it adds nothing to the merge.
+template <int NH, int D, int NS>
+__device__ __forceinline__ void store_empty(WaveStates<NH, D, NS>& st, int sl, int lane) {
+  if (lane < NH) {
+    st.m[sl][lane] = -INFINITY;
+    st.l[sl][lane] = 0.f;
+  }
+  for (int i = lane; i < NH * D; i += 64) st.o[sl][i / D][i % D] = 0.f;
+}
+
+// Q^T operand of one head group: head column lane % 16, dims 32*ks +
+// 8*(lane/16) .. +7; columns beyond the group's nh heads are zero padding.
+template <int D>
+__device__ __forceinline__ void load_q(u32x4 (&qb)[D / 32], const uint16_t* q_rows, int nh, int lane) {
+  const int hl = lane & 15;
+  if (hl < nh) {
+    const uint16_t* qp = q_rows + hl * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// One partition of one (sequence, head group) per item.  W physical waves
+// per workgroup run the partition's VW virtual waves.  With PAIR, a
+// partition of fewer than pair_blocks blocks is short enough that W / 2
+// waves suffice: the workgroup of an even head group then also takes the
+// next head group of the same sequence and partition, waves 0 .. W/2-1 on
+// one and W/2 .. W-1 on the other, and the odd head group's workgroup exits
+// at once.  The choice depends only on the partition's own length and does
+// not change the result (see SegmentWalk).  Two register pipelines of three
+// buffers each fit two waves per SIMD.
+template <class T, int D, int NH, int W, int VW, bool PAIR>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_partition_kernel(DecodeArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int VT = D / 16;
   constexpr int kThreads = 64 * W;
-  __shared__ float sm_m[W][NH];
-  __shared__ float sm_l[W][NH];
-  __shared__ float sm_o[W][NH][D];
+  constexpr int NITEM = PAIR ? 2 : 1;
+  static_assert(VW % W == 0 || (PAIR && VW % (W / 2) == 0), "virtual waves must split evenly");
+  __shared__ WaveStates<NH, D, VW> st[NITEM];
 
   // blockIdx.x = (part * num_seqs + s) * (num_kv_heads * num_sub) + head group
   const int n_hg = a.num_kv_heads * a.num_sub;
-  const int hg = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_hg));
+  const int hg0 = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_hg));
   const uint32_t rest = blockIdx.x / static_cast<uint32_t>(n_hg);
   const int s = static_cast<int>(rest % static_cast<uint32_t>(a.num_seqs));
   const int part = static_cast<int>(rest / static_cast<uint32_t>(a.num_seqs));
-  const int g = hg / a.num_sub;
-  const int sub = hg - g * a.num_sub;
-  const int hq0 = g * a.group + sub * 16;
-  const int nh = min(16, a.group - sub * 16);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane & 15;
-  const int quad = lane >> 4;
 
   const int L = a.context_lens[s];
   const int np = num_partitions(L, a);
   if (np <= 0) {
     // Empty context: zero rows.  Invalid length: NaN rows.  Partition 0 only.
     if (part == 0) {
+      const int g = hg0 / a.num_sub;
+      const int hq0 = g * a.group + (hg0 - g * a.num_sub) * 16;
+      const int nh = min(16, a.group - (hg0 - g * a.num_sub) * 16);
       const uint16_t fill = np == 0 ? uint16_t(0) : from_f32<T>(NAN);
       for (int i = tid; i < nh * D; i += kThreads)
         a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + i / D) * D + i % D] = fill;
@@ -280,110 +484,49 @@ void decode_partition_kernel(DecodeArgs a) {
   const int blk0 = partition_start(part, nb_seq, np);
   const int nblk = partition_start(part + 1, nb_seq, np) - blk0;   // 1 .. part_blocks
 
-  // This partition's block ids, 64 per register with one per lane
-  // (part_blocks <= 64 * kBtRegs).
-  int my_bt[kBtRegs];
-  bool bad_id = false;
-  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(s) * a.bt_stride + blk0;
-#pragma unroll
-  for (int r = 0; r < kBtRegs; ++r) {
-    my_bt[r] = 0;
-    if (64 * r < nblk) {                      // wave-uniform
-      const int jj = 64 * r + lane;
-      if (jj < nblk) my_bt[r] = bt_row[jj];
-      const bool bad = jj < nblk && (my_bt[r] < 0 || my_bt[r] >= a.num_blocks);
-      bad_id |= bad;
-      if (bad) my_bt[r] = 0;
-    }
-  }
+  const bool paired = PAIR && nblk < a.pair_blocks;
+  if (paired && (hg0 & 1)) return;            // taken by the even neighbour's workgroup
+  const int item = paired ? static_cast<int>(w >= W / 2) : 0;
+  const int pw = paired ? W / 2 : W;
+  const int wl = w - item * (W / 2) * static_cast<int>(paired);
+  const int hg = hg0 + item;
+  const bool active = hg < n_hg;              // an odd last head group leaves a half idle
+  const int g = hg / a.num_sub;
+  const int sub = hg - g * a.num_sub;
+  const int hq0 = g * a.group + sub * 16;
+  const int nh = min(16, a.group - sub * 16);
+
+  int bt[kBtRegs];
+  bool bad_id;
+  load_table(bt, a.block_tables + static_cast<int64_t>(s) * a.bt_stride + blk0, nblk, lane, a.num_blocks,
+             bad_id);
   const bool poison = __any(bad_id);
 
-  // Q^T operand: head column hl, dims 32*ks + 8*quad .. +7 (zero padding
-  // columns beyond the group).
-  u32x4 qb[KS];
-  if (hl < nh) {
-    const uint16_t* qp = a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0 + hl) * D + 8 * quad;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+  WaveStates<NH, D, VW>& my = st[item];
+  if (active) {
+    for (int v = wl; v < VW; v += pw)
+      if (v >= nblk) store_empty(my, v, lane);
+    u32x4 qb[D / 32];
+    load_q<D>(qb, a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0) * D, nh, lane);
+    const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+    const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+    const int hl = lane & 15, quad = lane >> 4;
+    const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
+    const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
+    auto pstart = [=](int p) { return blk0 + (p > 0 ? nblk : 0); };
+    const SegmentWalk<VW, decltype(pstart)> walk{1, 1, wl, pw, pstart};
+    run_wave<T, D, NH, VW, VW>(walk, 0, bt, blk0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, my);
   }
-
-  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
-  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
-  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
-  const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
-
-  float m_run = -INFINITY;   // running max of this lane's head (log2 units)
-  float l_run = 0.f;         // this lane's share of the running sum
-  f32x4 o[VT];
-#pragma unroll
-  for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto process = [&](BlockRegs<T, D>& cur, int j) __attribute__((always_inline)) {
-    process_block<T, D>(cur, L - (blk0 + j) * kBlock, qb, a.scale_log2, quad, m_run, l_run, o);
-  };
-
-  // Software pipeline over three register buffers: the loads of the next two
-  // blocks a wave handles are in flight while it works on the current one.
-  // Prefetches are issued unconditionally, so that the wait before each block
-  // only covers that block's own loads.  Past the end they read block 0 of
-  // the pool (the host rejects an empty pool when there is work): every
-  // wave's out-of-range prefetches share those lines, which then stay in L2,
-  // where re-reading a wave's own last block would go back to HBM under the
-  // non-temporal hint.
-  auto blk_off = [&](int jj) {
-    const int r = jj >> 6;                    // wave-uniform
-    int id = __builtin_amdgcn_readlane(my_bt[0], jj & 63);
-#pragma unroll
-    for (int k = 1; k < kBtRegs; ++k)
-      if (r == k) id = __builtin_amdgcn_readlane(my_bt[k], jj & 63);
-    return static_cast<int64_t>(id) * blk_elems;
-  };
-  int j = w;
-  auto pf_off = [&](int jj) -> int64_t { return jj < nblk ? blk_off(jj) : int64_t(0); };
-  if (j < nblk) {
-    BlockRegs<T, D> b0, b1, b2;
-    load_block<T, D>(b0, kbase, vbase, blk_off(j));
-    load_block<T, D>(b1, kbase, vbase, pf_off(j + W));
-    for (;;) {
-      load_block<T, D>(b2, kbase, vbase, pf_off(j + 2 * W));
-      process(b0, j);
-      j += W;
-      if (j >= nblk) break;
-      load_block<T, D>(b0, kbase, vbase, pf_off(j + 2 * W));
-      process(b1, j);
-      j += W;
-      if (j >= nblk) break;
-      load_block<T, D>(b1, kbase, vbase, pf_off(j + 2 * W));
-      process(b2, j);
-      j += W;
-      if (j >= nblk) break;
-    }
-  }
-
-  // Per-head sums over the four key groups of the wave.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (lane < NH) {
-    sm_m[w][lane] = m_run;
-    sm_l[w][lane] = l_run;
-  }
-#pragma unroll
-  for (int t = 0; t < VT; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = 4 * quad + e;
-      if (h < NH) sm_o[w][h][16 * t + hl] = o[t][e];
-    }
   __syncthreads();
 
-  for (int i = tid; i < nh * D; i += kThreads) {
+  if (!active) return;
+  const int t0 = paired ? tid - item * (kThreads / 2) : tid;
+  const int tn = paired ? kThreads / 2 : kThreads;
+  for (int i = t0; i < nh * D; i += tn) {
     const int h = i / D;
     const int d = i - h * D;
     float M, lsum, acc;
-    merge_waves<W, NH, D>(sm_m, sm_l, sm_o, h, d, M, lsum, acc);
+    merge_waves<VW, NH, D>(my.m, my.l, my.o, h, d, M, lsum, acc);
     if (poison) acc = NAN;
     const int64_t row = static_cast<int64_t>(s) * a.num_q_heads + hq0 + h;
     if (np == 1) {
@@ -402,36 +545,32 @@ void decode_partition_kernel(DecodeArgs a) {
 // Single-pass split-KV: one workgroup of NGRP * W waves takes every
 // partition of one (sequence, head group) and merges them on chip, so the
 // partition states never go through HBM.  Wave group gi = w / W takes
-// partitions gi, gi + NGRP, ...; inside a partition its W waves interleave
-// the blocks exactly as the W waves of decode_partition_kernel do (wave wl
-// takes blocks start + wl, start + wl + W, ...), each wave's state goes to
-// LDS, and the states are merged with the same code as the two-pass path
-// (merge_waves, then merge_partitions).  The result is therefore bit-identical
-// to decode_partition_kernel + decode_merge_kernel at the same partition size,
-// which keeps it independent of the batch the sequence is in.  Each wave's
-// register pipeline runs on across partition boundaries.  The whole block
-// table of the sequence sits in registers (at most 64 * kBtRegs blocks) and
-// at most PMAX partitions fit in LDS; the host only picks this kernel when
-// both hold.
-template <int W, int NH, int D, int NGRP>
+// partitions gi, gi + NGRP, ...; inside a partition its W waves run the VW
+// virtual waves exactly as decode_partition_kernel does, each segment's state
+// goes to LDS, and the states are merged with the same code as the two-pass
+// path (merge_waves, then merge_partitions).  The result is therefore
+// bit-identical to decode_partition_kernel + decode_merge_kernel at the same
+// partition size, which keeps it independent of the batch the sequence is
+// in.  Each wave's register pipeline runs on across partition boundaries.
+// The whole block table of the sequence sits in registers (at most 64 *
+// kBtRegs blocks) and at most PMAX partitions fit in LDS; the host only picks
+// this kernel when both hold.
+template <int VW, int NH, int D, int THREADS>
 constexpr int fused_max_parts() {
-  // LDS budget per workgroup: two 4-wave workgroups or one 8-wave workgroup
-  // per CU (160 KB).
-  constexpr int budget = W * NGRP <= 4 ? 78 * 1024 : 150 * 1024;
-  constexpr int per_part = (W * NH * (D + 2) + 2 * NH) * 4;
+  // LDS budget per workgroup: two 256-thread workgroups or one 512-thread
+  // workgroup per CU (160 KB).
+  constexpr int budget = THREADS <= 256 ? 78 * 1024 : 150 * 1024;
+  constexpr int per_part = (VW * NH * (D + 2) + 2 * NH) * 4;
   return budget / per_part < 32 ? budget / per_part : 32;
 }
 
-template <class T, int D, int NH, int W, int NGRP>
+template <class T, int D, int NH, int W, int NGRP, int VW>
 __global__ __launch_bounds__(64 * W * NGRP) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_fused_kernel(DecodeArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int VT = D / 16;
   constexpr int kThreads = 64 * W * NGRP;
-  constexpr int PMAX = fused_max_parts<W, NH, D, NGRP>();
-  __shared__ float sm_m[PMAX][W][NH];
-  __shared__ float sm_l[PMAX][W][NH];
-  __shared__ float sm_o[PMAX][W][NH][D];
+  constexpr int PMAX = fused_max_parts<VW, NH, D, kThreads>();
+  static_assert(VW % W == 0, "virtual waves must split evenly");
+  __shared__ WaveStates<NH, D, PMAX * VW> st;
   __shared__ float sm_ml[NH][PMAX][2];
 
   // blockIdx.x = s * num_kv_heads + KV head (one head sub-group: the host sends group <= 8)
@@ -444,8 +583,6 @@ void decode_fused_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gi = w / W;
   const int wl = w - gi * W;
-  const int hl = lane & 15;
-  const int quad = lane >> 4;
 
   const int L = a.context_lens[s];
   const int np = num_partitions(L, a);
@@ -458,169 +595,46 @@ void decode_fused_kernel(DecodeArgs a) {
   }
   const int nb_seq = (L + kBlock - 1) / kBlock;   // <= 64 * kBtRegs, np <= PMAX (host)
 
-  // The sequence's block ids, 64 per register with one per lane.
-  int my_bt[kBtRegs];
-  bool bad_id = false;
-  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(s) * a.bt_stride;
-#pragma unroll
-  for (int r = 0; r < kBtRegs; ++r) {
-    my_bt[r] = 0;
-    if (64 * r < nb_seq) {                    // wave-uniform
-      const int jj = 64 * r + lane;
-      if (jj < nb_seq) my_bt[r] = bt_row[jj];
-      const bool bad = jj < nb_seq && (my_bt[r] < 0 || my_bt[r] >= a.num_blocks);
-      bad_id |= bad;
-      if (bad) my_bt[r] = 0;
-    }
-  }
-  // A bad id anywhere poisons the sequence's row, as it does through the
-  // merge of the two-pass path (every wave holds the whole table).
+  // The sequence's block ids; a bad id anywhere poisons the sequence's row,
+  // as it does through the merge of the two-pass path.
+  int bt[kBtRegs];
+  bool bad_id;
+  load_table(bt, a.block_tables + static_cast<int64_t>(s) * a.bt_stride, nb_seq, lane, a.num_blocks, bad_id);
   const bool poison = __any(bad_id);
-
-  u32x4 qb[KS];
-  if (hl < nh) {
-    const uint16_t* qp = a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0 + hl) * D + 8 * quad;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
-  }
-
-  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
-  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
-  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
-  const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
-
-  // Partitions this wave has no block in keep the empty state (max -inf,
-  // sum 0, accumulator 0), as the idle waves of a short partition do in the
-  // two-pass kernel.  Every slot written here belongs to this wave alone, and
-  // LDS writes of one wave land in program order, so the states stored below
-  // overwrite these.
-  for (int p = gi; p < np; p += NGRP) {
-    if (lane < NH) {
-      sm_m[p][wl][lane] = -INFINITY;
-      sm_l[p][wl][lane] = 0.f;
-    }
-    for (int i = lane; i < NH * D; i += 64) sm_o[p][wl][i / D][i % D] = 0.f;
-  }
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 o[VT];
-#pragma unroll
-  for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Lane p holds the first block of partition p (p <= np < 64).
   const int start_lane = partition_start(min(lane, np), nb_seq, np);
-  auto pstart = [&](int p) { return __builtin_amdgcn_readlane(start_lane, p); };
-  // A cursor (p, j) is this wave's block j (absolute index in the sequence)
-  // of partition p; p >= np once the wave has no more blocks.
-  auto settle = [&](int& p, int& j) {
-    while (p < np && j >= pstart(p + 1)) {
-      p += NGRP;
-      if (p < np) j = pstart(p) + wl;
-    }
-  };
-  auto advance = [&](int& p, int& j) {
-    if (p < np) {
-      j += W;
-      settle(p, j);
-    }
-  };
-  auto blk_off = [&](int jj) {
-    const int r = jj >> 6;                    // wave-uniform
-    int id = __builtin_amdgcn_readlane(my_bt[0], jj & 63);
-#pragma unroll
-    for (int k = 1; k < kBtRegs; ++k)
-      if (r == k) id = __builtin_amdgcn_readlane(my_bt[k], jj & 63);
-    return static_cast<int64_t>(id) * blk_elems;
-  };
-  // Past the end, prefetches read block 0 of the pool, as in the two-pass kernel.
-  auto pf_off = [&](int p, int j) -> int64_t { return p < np ? blk_off(j) : int64_t(0); };
+  auto pstart = [=](int p) { return __builtin_amdgcn_readlane(start_lane, p); };
+  for (int p = gi; p < np; p += NGRP)
+    for (int v = wl; v < VW; v += W)
+      if (v >= pstart(p + 1) - pstart(p)) store_empty(st, p * VW + v, lane);
 
-  // The wave's state for partition pc goes to LDS when its first block of a
-  // later partition comes up, and after the loop.  Same store as after the
-  // loop of decode_partition_kernel.
-  int pc = -1;
-  auto flush = [&]() {
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (lane < NH) {
-      sm_m[pc][wl][lane] = m_run;
-      sm_l[pc][wl][lane] = l_run;
-    }
-#pragma unroll
-    for (int t = 0; t < VT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int h = 4 * quad + e;
-        if (h < NH) sm_o[pc][wl][h][16 * t + hl] = o[t][e];
-      }
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int t = 0; t < VT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  auto process = [&](BlockRegs<T, D>& cur, int p, int j) __attribute__((always_inline)) {
-    if (p != pc) {
-      if (pc >= 0) flush();
-      pc = p;
-    }
-    process_block<T, D>(cur, L - j * kBlock, qb, a.scale_log2, quad, m_run, l_run, o);
-  };
-
-  // Three register buffers, two blocks in flight, as in the two-pass kernel;
-  // c0 is the cursor of the block being processed, c1 and c2 of the next two.
-  int p0 = gi, j0 = 0;
-  if (p0 < np) j0 = pstart(p0) + wl;
-  settle(p0, j0);
-  if (p0 < np) {
-    int p1 = p0, j1 = j0;
-    advance(p1, j1);
-    int p2 = p1, j2 = j1;
-    advance(p2, j2);
-    BlockRegs<T, D> b0, b1, b2;
-    load_block<T, D>(b0, kbase, vbase, blk_off(j0));
-    load_block<T, D>(b1, kbase, vbase, pf_off(p1, j1));
-    auto shift = [&]() {
-      p0 = p1; j0 = j1;
-      p1 = p2; j1 = j2;
-      advance(p2, j2);
-    };
-    for (;;) {
-      load_block<T, D>(b2, kbase, vbase, pf_off(p2, j2));
-      process(b0, p0, j0);
-      shift();
-      if (p0 >= np) break;
-      load_block<T, D>(b0, kbase, vbase, pf_off(p2, j2));
-      process(b1, p0, j0);
-      shift();
-      if (p0 >= np) break;
-      load_block<T, D>(b1, kbase, vbase, pf_off(p2, j2));
-      process(b2, p0, j0);
-      shift();
-      if (p0 >= np) break;
-    }
-    flush();
-  }
+  u32x4 qb[D / 32];
+  load_q<D>(qb, a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0) * D, nh, lane);
+  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+  const int hl = lane & 15, quad = lane >> 4;
+  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
+  const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
+  const SegmentWalk<VW, decltype(pstart)> walk{NGRP, np, wl, W, pstart};
+  run_wave<T, D, NH, PMAX * VW, VW>(walk, gi, bt, 0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
   __syncthreads();
 
-  // Per partition, the W wave states merged (same code as the two-pass
-  // kernel).  A partition's accumulator replaces its wave-0 state in place:
-  // the element (p, 0, h, d) is read only by the thread that writes it.
+  // Per partition, the VW virtual-wave states merged (same code as the
+  // two-pass kernel).  A partition's accumulator replaces its first state in
+  // place: the element (p * VW, h, d) is read only by the thread that writes it.
   for (int i = tid; i < np * nh * D; i += kThreads) {
     const int p = i / (nh * D);
     const int r = i - p * (nh * D);
     const int h = r / D;
     const int d = r - h * D;
     float M, lsum, acc;
-    merge_waves<W, NH, D>(sm_m[p], sm_l[p], sm_o[p], h, d, M, lsum, acc);
+    merge_waves<VW, NH, D>(st.m + p * VW, st.l + p * VW, st.o + p * VW, h, d, M, lsum, acc);
     if (poison) acc = NAN;
     if (np == 1) {
       a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + h) * D + d] = from_f32<T>(acc / lsum);
     } else {
-      sm_o[p][0][h][d] = acc;
+      st.o[p * VW][h][d] = acc;
       if (d == 0) {
         sm_ml[h][p][0] = M;
         sm_ml[h][p][1] = lsum;
@@ -633,7 +647,7 @@ void decode_fused_kernel(DecodeArgs a) {
   // The partitions merged per query head, one wave per head (the merge
   // pass's code, reading LDS instead of the workspace).
   for (int h = w; h < nh; h += W * NGRP)
-    merge_partitions<T, D>(&sm_ml[h][0][0], &sm_o[0][0][h][0], static_cast<int64_t>(W) * NH * D, np, lane,
+    merge_partitions<T, D>(&sm_ml[h][0][0], &st.o[0][h][0], static_cast<int64_t>(VW) * NH * D, np, lane,
                            a.out + (static_cast<int64_t>(s) * a.num_q_heads + hq0 + h) * D);
 }
 
@@ -663,38 +677,45 @@ int merge_kind_nh(const DecodeArgs& a) {
     return kMergeTwoPass;
   } else {
     if (a.fuse_groups <= 0 || a.num_sub != 1) return kMergeTwoPass;
-    const int cap = a.waves == 8            ? fused_max_parts<8, NH, D, 1>()
-                    : a.fuse_groups == 2    ? fused_max_parts<4, NH, D, 2>()
-                                            : fused_max_parts<4, NH, D, 1>();
+    const int cap = a.waves == 8 ? fused_max_parts<8, NH, D, 512>() : fused_max_parts<4, NH, D, 512>();
     return a.max_parts <= cap ? kMergeOnChip : kMergeTwoPass;
   }
 }
 
-template <class T, int D, int NH, int W, int NGRP>
-void launch_fused(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_kv_heads));
-  hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, W, NGRP>), grid, dim3(64 * W * NGRP), 0, stream, a);
+template <class T, int D, int NH, int W, int VW, bool PAIR>
+void launch_partition(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, W, VW, PAIR>), dim3(static_cast<uint32_t>(n_wg)),
+                     dim3(64 * W), 0, stream, a);
 }
 
 template <class T, int D, int NH>
 hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
   if constexpr (NH <= 8) {
     if (merge_kind_nh<D, NH>(a) == kMergeOnChip) {
+      // One workgroup per (sequence, KV head): 8 waves on the 8 virtual waves
+      // of long partitions, or two groups of 4 waves taking alternate short
+      // partitions.
+      const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_kv_heads));
       if (a.waves == 8)
-        launch_fused<T, D, NH, 8, 1>(a, stream);
-      else if (a.fuse_groups == 2)
-        launch_fused<T, D, NH, 4, 2>(a, stream);
+        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, 8, 1, 8>), grid, dim3(512), 0, stream, a);
       else
-        launch_fused<T, D, NH, 4, 1>(a, stream);
+        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, 4, 2, 4>), grid, dim3(512), 0, stream, a);
       return hipGetLastError();
     }
   }
-  const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
-  const dim3 grid(static_cast<uint32_t>(n_wg));
-  if (a.waves == 8)
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 8>), grid, dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 4>), grid, dim3(256), 0, stream, a);
+  if (a.waves == 4) {
+    launch_partition<T, D, NH, 4, 4, false>(a, stream);
+  } else if (a.launch_waves == 4) {
+    launch_partition<T, D, NH, 4, 8, false>(a, stream);
+  } else if (a.pair_blocks > 0) {
+    if constexpr (NH <= 4)
+      launch_partition<T, D, NH, 8, 8, true>(a, stream);
+    else
+      launch_partition<T, D, NH, 8, 8, false>(a, stream);
+  } else {
+    launch_partition<T, D, NH, 8, 8, false>(a, stream);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;

@@ -41,7 +41,7 @@ struct DecodeArgs {
   float* ws_ml;               // [S][Hq][max_parts][2]  (max in log2 units, sum)
   const uint16_t* q;          // [S][Hq][D]
   const uint16_t* k_cache;    // [N][Hkv][D/32][16][32]
-  const uint16_t* v_cache;    // [N][Hkv][D][16]
+  const uint16_t* v_cache;    // [N][Hkv][4][D][4]
   const int32_t* block_tables;
   const int32_t* context_lens;
   int64_t num_blocks;
@@ -54,7 +54,9 @@ struct DecodeArgs {
   int32_t part_blocks;        // partition size in blocks
   int32_t max_parts;
   int32_t max_context_len;
-  int32_t waves;              // waves sharing one partition (4 or 8)
+  int32_t waves;              // virtual waves interleaving a partition's blocks (4 or 8): the reduction order
+  int32_t launch_waves;       // physical waves per workgroup of the two-pass kernel (speed only)
+  int32_t pair_blocks;        // > 0: a partition of fewer blocks runs on half the waves, two head groups per workgroup
   int32_t fuse_groups;        // > 0: single pass, partitions merged on chip by this many wave groups
   float scale_log2;           // scale * log2(e)
 };
@@ -62,8 +64,8 @@ struct DecodeArgs {
 struct PrefillArgs {
   uint16_t* out;              // [T][Hq][D]
   const uint16_t* q;          // [T][Hq][D]
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const uint16_t* k_cache;    // [N][Hkv][D/32][16][32]
+  const uint16_t* v_cache;    // [N][Hkv][4][D][4]
   const int32_t* block_tables;
   const int32_t* q_start_loc;
   const int32_t* seq_lens;

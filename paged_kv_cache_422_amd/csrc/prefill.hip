@@ -81,10 +81,7 @@ __device__ __forceinline__ int swap_bits23(int r) {
 constexpr int kPrefillWaves = 8;
 constexpr int kXcds = 8;              // MI355X: 8 XCDs, 32 CUs and one L2 each
 constexpr float kLazyLog2 = 8.f;      // running-maximum slack, log2 units
-#ifndef PF_PREFETCH
-#define PF_PREFETCH 4
-#endif
-constexpr int kPrefetch = PF_PREFETCH;   // LDS operand reads in flight ahead of the MFMAs
+constexpr int kPrefetch = 4;          // LDS operand reads in flight ahead of the MFMAs
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
 template <class T, int D>
