@@ -200,6 +200,30 @@ pa_status pa_decode(void* out, const void* q,
                     pa_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_decode without allocation, for callers that cannot allocate device
+ * memory or pass one in: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results (bit for bit)
+ * and errors as pa_decode, without the workspace: when the partitions are
+ * merged in two passes their states go to a static scratch array of
+ * PA_DECODE_STATIC_SCRATCH_BYTES that the library holds on each device it
+ * runs on until the process ends.  A call that would need more returns
+ * PA_ENOTSUP before launching anything; the single pass, and calls with one
+ * partition per sequence, need none.  The scratch of the current device is
+ * used, so `stream` must belong to it.  Every call on one device shares that
+ * scratch: calls that may overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller.  The call allocates
+ * nothing; its first use on a device looks the scratch's address up once.
+ * ---------------------------------------------------------------------- */
+#define PA_DECODE_STATIC_SCRATCH_BYTES (16u << 20)
+pa_status pa_decode_static(void* out, const void* q,
+                           const void* k_cache, const void* v_cache, int64_t num_blocks,
+                           const int32_t* block_tables, int32_t bt_stride,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_context_len, float scale,
+                           int32_t partition_size, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Chunked prefill: the scheduler serves decode first and fills the rest of
  * the step's token budget with prefill chunks ("PagedAttention in vLLM: A
  * Throughput Settings Guide", section "Tuning Batching, Prefill, and Cache").

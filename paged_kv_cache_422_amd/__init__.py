@@ -35,6 +35,7 @@ PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_ENOTSUP = range(5)
 PA_POOL_PREFIX_CACHING = 1          # pa_pool_create_ex flag
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1      # pa_swap_blocks directions
 PA_FP16, PA_BF16 = 0, 1
+DECODE_STATIC_SCRATCH_BYTES = 16 << 20   # PA_DECODE_STATIC_SCRATCH_BYTES
 _STATUS = {1: "EINVAL", 2: "ENOMEM", 3: "EHIP", 4: "ENOTSUP"}
 
 c_i32, c_i64, c_u64, c_f32, c_sz, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
@@ -54,6 +55,8 @@ _SIGS = {
     "pa_decode_plan": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, P_i32, P_i32, P_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_i32, c_vp]),
+    "pa_decode_static": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
+                                 c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "pa_pool_create": (c_i32, [c_i32, c_i32, c_u64, ctypes.POINTER(c_vp)]),
@@ -225,6 +228,20 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len
                           _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
                           Hkv, D, B, max_context_len, scale, partition_size, _ptr(workspace),
                           ws_bytes, _dtype_code(q), _stream(stream)))
+    return out
+
+
+def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                  partition_size=0, stream=None):
+    """decode() without a workspace: two-pass partition states go to the
+    library's static per-device scratch (PA_DECODE_STATIC_SCRATCH_BYTES);
+    nothing is allocated.  Calls that overlap on one device race."""
+    S, Hq, D = q.shape
+    N, Hkv, B, _ = _cache_dims(k_cache, v_cache)
+    _check(_lib.pa_decode_static(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
+                                 Hkv, D, B, max_context_len, scale, partition_size, _dtype_code(q),
+                                 _stream(stream)))
     return out
 
 

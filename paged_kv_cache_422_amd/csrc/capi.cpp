@@ -262,49 +262,72 @@ pa_status pa_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_h
   return ok();
 }
 
-pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                    int32_t max_context_len, float scale, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  const char* fn = "pa_decode";
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_decode_static: the same checks and kernels; the split-KV
+// workspace comes from the caller (pa_decode) or from this device's static
+// scratch (from_scratch), which is only needed, and only looked up, when the
+// partitions are merged in two passes.
+pa_status decode_call(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                      int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_context_len, float scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, bool from_scratch,
+                      pa_dtype dtype, void* stream) {
+  const std::string f(fn);
   if (pa_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype)) return st;
   if (num_seqs < 0 || num_blocks < 0 || bt_stride <= 0 || max_context_len < 0)
-    return fail(PA_EINVAL, "pa_decode: negative size or bt_stride <= 0");
+    return fail(PA_EINVAL, f + ": negative size or bt_stride <= 0");
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(PA_EINVAL, "pa_decode: num_q_heads must be a positive multiple of num_kv_heads");
+    return fail(PA_EINVAL, f + ": num_q_heads must be a positive multiple of num_kv_heads");
   if (partition_size != 0 &&
       (partition_size % kBlock != 0 || partition_size < kBlock || partition_size > kMaxPartitionTokens))
-    return fail(PA_ENOTSUP, "pa_decode: partition_size must be 0 or a multiple of 16 in [16, 4096]");
+    return fail(PA_ENOTSUP, f + ": partition_size must be 0 or a multiple of 16 in [16, 4096]");
   if (num_seqs == 0) return ok();
   // A bad block id, and a prefetch past a sequence's last block, read block 0.
-  if (num_blocks == 0) return fail(PA_EINVAL, "pa_decode: num_blocks must be positive when num_seqs > 0");
+  if (num_blocks == 0) return fail(PA_EINVAL, f + ": num_blocks must be positive when num_seqs > 0");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PA_EINVAL, "pa_decode: null pointer");
+    return fail(PA_EINVAL, f + ": null pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(PA_ENOTSUP, "pa_decode: 16-byte alignment required");
-  if (num_seqs > 65535) return fail(PA_ENOTSUP, "pa_decode: at most 65535 sequences per call");
+    return fail(PA_ENOTSUP, f + ": 16-byte alignment required");
+  if (num_seqs > 65535) return fail(PA_ENOTSUP, f + ": at most 65535 sequences per call");
   const int32_t P = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                       max_context_len);
-  size_t need = 0;
-  if (pa_status st = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                              P, num_kv_heads, &need))
-    return st;
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PA_EINVAL, "pa_decode: workspace too small (need " + std::to_string(need) +
-                               " bytes, got " + std::to_string(workspace_bytes) + ")");
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t num_sub = (group + 15) / 16;
   const int64_t max_parts = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P);
   // One workgroup of 256 work-items per (partition, sequence, head group);
   // the launch's work-item count must fit the dispatch packet's 32 bits.
   if (max_parts * num_seqs * num_kv_heads * num_sub * 256 > static_cast<int64_t>(UINT32_MAX))
-    return fail(PA_ENOTSUP, "pa_decode: too many (partition, sequence, head) work items");
+    return fail(PA_ENOTSUP, f + ": too many (partition, sequence, head) work items");
   pa::DecodeArgs a{};
+  fill_decode_plan(a, num_seqs, num_q_heads, num_kv_heads, P, max_context_len);
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * max_parts;
+  size_t need = 0;
+  if (from_scratch) {
+    if (pa::decode_merge_kind(a, head_dim) == pa::kMergeTwoPass)
+      need = static_cast<size_t>(rows) * (head_dim + 2) * sizeof(float);
+    if (need > PA_DECODE_STATIC_SCRATCH_BYTES)
+      return fail(PA_ENOTSUP, f + ": the partition states need " + std::to_string(need) +
+                                  " bytes, more than the static scratch's " +
+                                  std::to_string(PA_DECODE_STATIC_SCRATCH_BYTES) +
+                                  " (use pa_decode with a workspace, or larger partitions)");
+    if (need > 0) {
+      hipError_t e = pa::static_scratch(&workspace);
+      if (e != hipSuccess) return fail(PA_EHIP, f + ": static scratch: " + hipGetErrorString(e));
+    }
+  } else {
+    if (pa_status st = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, P,
+                                                num_kv_heads, &need))
+      return st;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(PA_EINVAL, f + ": workspace too small (need " + std::to_string(need) + " bytes, got " +
+                                 std::to_string(workspace_bytes) + ")");
+  }
   a.out = static_cast<uint16_t*>(out);
   float* ws = static_cast<float*>(workspace);
-  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * max_parts;
   a.ws_acc = need ? ws : nullptr;
   a.ws_ml = need ? ws + rows * head_dim : nullptr;
   a.q = static_cast<const uint16_t*>(q);
@@ -314,9 +337,34 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.context_lens = context_lens;
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
-  fill_decode_plan(a, num_seqs, num_q_heads, num_kv_heads, P, max_context_len);
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_result(fn, pa::launch_decode(a, head_dim, dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  return decode_call("pa_decode", out, q, k_cache, v_cache, num_blocks, block_tables, bt_stride, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, false, dtype, stream);
+}
+
+pa_status pa_decode_static(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           int64_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_context_len, float scale, int32_t partition_size, pa_dtype dtype,
+                           void* stream) {
+  return decode_call("pa_decode_static", out, q, k_cache, v_cache, num_blocks, block_tables, bt_stride,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                     scale, partition_size, nullptr, 0, true, dtype, stream);
 }
 
 pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,

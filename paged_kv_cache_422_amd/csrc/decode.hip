@@ -47,8 +47,20 @@
 // Query-head columns beyond the group size are zero padding.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
+#include "pa.h"
+
+// Split-KV partition states of pa_decode_static, for callers that cannot
+// allocate device memory: a fixed array that every device the library runs
+// on holds from the first use until the process ends.  Host code never names
+// it as an address; it uses the device address that static_scratch() looks
+// up per device.  Every call on one device shares it, so calls that overlap
+// on one device race.  Nothing in it needs clearing: each state the merge
+// pass reads was written earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_STATIC_SCRATCH_BYTES];
 
 namespace pa {
 
@@ -753,6 +765,26 @@ int merge_kind_d(const DecodeArgs& a) {
 }
 
 }  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // The symbol resolves to the copy on the current device, which is dev.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int decode_merge_kind(const DecodeArgs& a, int head_dim) {
   return head_dim == 64 ? merge_kind_d<64>(a) : merge_kind_d<128>(a);

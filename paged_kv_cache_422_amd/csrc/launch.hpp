@@ -88,5 +88,8 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int dtype, hipStream
 enum { kMergeNone = 0, kMergeOnChip = 1, kMergeTwoPass = 2 };
 int decode_merge_kind(const DecodeArgs& a, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int dtype, hipStream_t stream);
+// Device address of the current device's copy of the library's static decode
+// scratch (PA_DECODE_STATIC_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t static_scratch(void** ptr);
 
 }  // namespace pa

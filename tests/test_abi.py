@@ -436,3 +436,23 @@ def test_swap_blocks_rejects_before_launch(direction, aligned, code):
     f = ctypes.c_void_p(0x1000 if aligned else 0x1008)
     st_ = pa._lib.pa_swap_blocks(f, f, 10, f, f, 10, f, 3, direction, 8, 128, 16, pa.PA_BF16, None)
     assert st_ == code, pa.last_error()
+
+
+def test_decode_static_rejects_before_launch():
+    """pa_decode_static checks everything pa_decode does, and refuses a call
+    whose two-pass partition states would not fit its static scratch, before
+    touching the device (so these run without one)."""
+    m = re.search(r"#define PA_DECODE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                  open(os.path.join(ROOT, "include", "pa.h")).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.DECODE_STATIC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x1000)
+    # 4096 sequences x 32 heads x 64 partitions of 16 tokens: 4096*32*64*130*4 bytes
+    st_ = pa._lib.pa_decode_static(fake, fake, fake, fake, 100, fake, 64, fake, 4096, 32, 8, 128, 16,
+                                   1024, 0.1, 16, pa.PA_BF16, None)
+    assert st_ == pa.PA_ENOTSUP and "static scratch" in pa.last_error()
+    assert pa._lib.pa_decode_static(None, None, None, None, 100, None, 16, None, 4, 32, 8, 128, 16, 256,
+                                    0.1, 0, pa.PA_BF16, None) == pa.PA_EINVAL
+    assert pa._lib.pa_decode_static(None, None, None, None, 0, None, 1, None, 0, 8, 8, 64, 16, 0, 1.0, 0,
+                                    0, None) == pa.PA_OK
+    assert pa._lib.pa_decode_static(fake, fake, fake, fake, 100, fake, 16, fake, 4, 8, 8, 96, 16, 16,
+                                    0.1, 0, pa.PA_FP16, None) == pa.PA_ENOTSUP
