@@ -164,12 +164,13 @@ def decode_logical(q, K_seqs, V_seqs, scale: float, dtype: str) -> np.ndarray:
 
 def prefill(q, k_cache, v_cache, block_tables, q_start_loc, seq_lens,
             scale: float, dtype: str, block_size: int = 16,
-            rows=None) -> np.ndarray:
+            rows=None, heads=None) -> np.ndarray:
     """Causal chunked-prefill attention over paged K/V, fp64, unrounded.
 
     q [T, Hq, D] packed; chunk c owns rows q_start_loc[c] .. q_start_loc[c+1]
     and block-table row c.  ``rows`` optionally restricts the work to a list
-    of packed row indices (others stay zero).
+    of packed row indices, ``heads`` to a list of query heads (the rest stay
+    zero); the restriction selects work and changes no arithmetic.
     """
     qf = widen(q, dtype)
     T, Hq, D = qf.shape
@@ -178,6 +179,7 @@ def prefill(q, k_cache, v_cache, block_tables, q_start_loc, seq_lens,
     sc = scale64(scale)
     out = np.zeros((T, Hq, D), dtype=np.float64)
     want = None if rows is None else set(int(r) for r in rows)
+    want_h = None if heads is None else set(int(h) for h in heads)
     n_chunks = len(seq_lens)
     for c in range(n_chunks):
         r0, r1 = int(q_start_loc[c]), int(q_start_loc[c + 1])
@@ -185,6 +187,9 @@ def prefill(q, k_cache, v_cache, block_tables, q_start_loc, seq_lens,
         n_keys = int(seq_lens[c])
         n_cached = n_keys - n
         for g in range(Hkv):
+            hs = [h for h in range(g * G, (g + 1) * G) if want_h is None or h in want_h]
+            if not hs:
+                continue
             K, V = gather_kv(k_cache, v_cache, block_tables[c], n_keys, g,
                              block_size, dtype)
             for j in range(n):
@@ -192,7 +197,7 @@ def prefill(q, k_cache, v_cache, block_tables, q_start_loc, seq_lens,
                 if want is not None and r not in want:
                     continue
                 lim = n_cached + j + 1
-                for h in range(g * G, (g + 1) * G):
+                for h in hs:
                     out[r, h] = attend(qf[r, h], K[:lim], V[:lim], sc)
     return out
 

@@ -135,7 +135,7 @@ void prefill_kernel(PrefillArgs a) {
   const int n = a.q_start_loc[c + 1] - r_start;
   const int L = a.seq_lens[c];
   const int n_cached = L - n;
-  if (n <= 0 || n > a.max_q_len) return;     // nothing addressable to write
+  if (n <= 0) return;                        // empty chunk
   const int wg_row0 = rb * wg_rows;
   if (wg_row0 >= n) return;                  // whole workgroup past the chunk
   const int row0 = wg_row0 + rt * 32;
@@ -144,7 +144,10 @@ void prefill_kernel(PrefillArgs a) {
   const bool row_ok = my_row < n;
   const int64_t out_row = (static_cast<int64_t>(r_start) + my_row) * a.num_q_heads + hq;
 
-  const bool bad_len = n_cached < 0 || L > a.max_seq_len || L > a.bt_stride * kBlock;
+  // A chunk longer than max_q_len (the grid covers only that many rows per
+  // chunk) or a length outside the host's bounds gets NaN in every row the
+  // grid covers.
+  const bool bad_len = n > a.max_q_len || n_cached < 0 || L > a.max_seq_len || L > a.bt_stride * kBlock;
   if (bad_len) {
     if (row_ok) {
       const uint16_t nanv = from_f32<T>(NAN);

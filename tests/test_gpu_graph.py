@@ -1,15 +1,18 @@
 """The mixed step (slot-mapped write, prefill chunks, split-KV decode with
 its partitions merged by a second kernel, or on chip in one pass) captured
-into a HIP graph: every replay, with the program's own eager work and
-synchronisations in between, reproduces the eager step bit for bit.  All
-three calls enqueue on the caller's stream, take their workspace from the
-caller and never allocate or set memory, so they can be captured."""
+into a HIP graph: the eager step matches the fp64 oracle, and every replay,
+with the program's own eager work and synchronisations in between,
+reproduces the eager step bit for bit.  All three calls enqueue on the
+caller's stream, take their workspace from the caller and never allocate or
+set memory, so they can be captured."""
 import pytest
 import torch
 
 import paged_kv_cache_422_amd as pa
 import workloads as W
-from tests.gpu_util import DEV
+from oracle import attention as A
+from oracle import kv_cache as KC
+from tests.gpu_util import DEV, assert_close, bits
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +48,16 @@ def test_mixed_step_graph_replays_match_eager(P, merge):
     step()
     torch.cuda.synchronize()
     want = [t.clone() for t in (kc, vc, out_pre, out_dec)]
+
+    # The eager step against the oracle: the write bit for bit, prefill and
+    # decode within tolerance (so every replay below is held to it too).
+    kh, vh = bits(kc0), bits(vc0)
+    KC.write_kv(kh, vh, bits(k_new), bits(v_new), w.slot_mapping, 16)
+    assert (bits(kc).view('u2') == kh.view('u2')).all() and (bits(vc).view('u2') == vh.view('u2')).all()
+    assert_close(out_pre, A.prefill(bits(q_pre), kh, vh, w.prefill_bt, w.q_start_loc, w.prefill_seq_lens,
+                                    w.scale, w.dtype), what=f"eager prefill, P={P}")
+    assert_close(out_dec, A.decode(bits(q_dec), kh, vh, w.decode_bt, w.decode_lens, w.scale, w.dtype),
+                 what=f"eager decode, P={P}")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

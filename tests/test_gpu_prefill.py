@@ -165,34 +165,62 @@ def test_mixed_step_small():
 
 
 def test_mixed_step_full_size_sampled():
-    """The full 8192-token step (44 GB pool); oracle on sampled sequences and
-    rows, copying back only their blocks."""
+    """The full 8192-token step (44 GB pool).  The oracle takes every row of
+    both 2048-row chunks for the four query heads of one KV group (so every
+    prefill workgroup of that group is compared), and 256 seeded decode
+    sequences with all their heads, on copies of only the blocks they read."""
     w = mixed()
     print(f"mixed full: blocks={w.num_blocks}", flush=True)
     kc, vc, k_new, v_new, q_dec, q_pre = w.make_tensors(DEV)
     rng = np.random.default_rng(99)
-    dec_seqs = sorted(rng.choice(w.num_decode, 48, replace=False).tolist())
-    pre_rows = sorted(rng.choice(w.num_chunks * w.prefill_chunk, 48, replace=False).tolist())
+    dec_seqs = sorted(rng.choice(w.num_decode, 256, replace=False).tolist())
+    G = w.num_q_heads // w.num_kv_heads
+    g = int(rng.integers(w.num_kv_heads))
+    heads = list(range(g * G, (g + 1) * G))
     need = set()
     for s in dec_seqs:
         need.update(w.decode_bt[s, :-(-int(w.decode_lens[s]) // 16)].tolist())
     for c in range(w.num_chunks):
         need.update(w.prefill_bt[c, :-(-int(w.prefill_seq_lens[c]) // 16)].tolist())
     need = np.array(sorted(need), dtype=np.int64)
-    remap = {int(b): i for i, b in enumerate(need)}
+    remap = np.zeros(w.num_blocks, dtype=np.int64)       # unused entries read block 0
+    remap[need] = np.arange(len(need))
     idx = torch.from_numpy(need).to(DEV)
     kc_s, vc_s = bits(kc[idx]), bits(vc[idx])          # pre-step copies of the needed blocks
     out_pre, out_dec = _mixed_step(w, kc, vc, k_new, v_new, q_dec, q_pre)
-    print("  kernels done, running oracle", flush=True)
-    # Re-express the workload over the compacted block set for the oracle.
-    sm = np.array([remap.get(int(s) // 16, -1) * 16 + int(s) % 16 if int(s) // 16 in remap else -1
-                   for s in w.slot_mapping], dtype=np.int64)
-    dbt = np.vectorize(lambda b: remap.get(int(b), 0))(w.decode_bt).astype(np.int32)
-    pbt = np.vectorize(lambda b: remap.get(int(b), 0))(w.prefill_bt).astype(np.int32)
+    print(f"  kernels done; oracle on {len(need)} blocks, KV group {g}", flush=True)
+    # Re-express the workload over the compacted block set for the oracle:
+    # slots outside it are skipped, table entries map to their copies.
+    in_set = np.zeros(w.num_blocks, dtype=bool)
+    in_set[need] = True
+    blk = w.slot_mapping // 16
+    sm = np.where(in_set[blk], remap[blk] * 16 + w.slot_mapping % 16, -1).astype(np.int64)
+    dbt = remap[w.decode_bt].astype(np.int32)
+    pbt = remap[w.prefill_bt].astype(np.int32)
     kh, vh = kc_s.copy(), vc_s.copy()
     KC.write_kv(kh, vh, bits(k_new), bits(v_new), sm, 16)
     pre = A.prefill(bits(q_pre), kh, vh, pbt, w.q_start_loc, w.prefill_seq_lens, w.scale,
-                    w.dtype, rows=pre_rows)
+                    w.dtype, heads=heads)
     dec = A.decode(bits(q_dec), kh, vh, dbt, w.decode_lens, w.scale, w.dtype, seqs=dec_seqs)
-    assert_close(out_pre[pre_rows], pre[pre_rows], what="full mixed prefill (sampled rows)")
-    assert_close(out_dec[dec_seqs], dec[dec_seqs], what="full mixed decode (sampled seqs)")
+    assert_close(out_pre[:, heads], pre[:, heads], what=f"full mixed prefill (all rows, KV group {g})")
+    assert_close(out_dec[dec_seqs], dec[dec_seqs], what="full mixed decode (256 sequences)")
+
+
+def test_prefill_chunk_longer_than_max_q_len():
+    """A chunk with more rows than max_q_len gets NaN in every row the grid
+    covers and leaves the rows beyond untouched; the other chunks of the call
+    are unaffected."""
+    chunks = [(10, 40), (5, 100), (0, 30)]
+    q, kc, vc, bt, qsl, lens = prefill_case(chunks, 8, 2, 128, torch.float16, seed=4)
+    out = torch.full_like(q, 7.0)
+    pa.prefill_chunk(out, q, kc, vc, torch.from_numpy(bt).to(DEV), torch.from_numpy(qsl).to(DEV),
+                     torch.from_numpy(lens).to(DEV), 64, int(lens.max()), 0.088)
+    torch.cuda.synchronize()
+    covered = 64           # 8 waves over 4 query heads: two 32-row tiles per workgroup, one row block
+    r0 = int(qsl[1])
+    assert torch.isnan(out[r0:r0 + covered].float()).all()
+    assert (out[r0 + covered:int(qsl[2])].float() == 7.0).all()
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, 0.088, "fp16")
+    for c in (0, 2):
+        a, b = int(qsl[c]), int(qsl[c + 1])
+        assert_close(out[a:b], want[a:b], what=f"chunk {c} beside an over-long chunk")
