@@ -137,7 +137,12 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
 /* ------------------------------------------------------------------------
  * Paged decode attention: one query token per sequence attends to all
  * context_lens[s] keys of its sequence (the newest token's K/V must already be
- * written).  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * written), read through the sequence's block table as if its blocks were
+ * contiguous ("Inside vLLM ...", section "PagedAttention: What the OS Figured
+ * Out Decades Ago").  This step is bound by memory bandwidth ("PagedAttention
+ * in vLLM: A Throughput Settings Guide", section "Continuous Batching Keeps
+ * the GPU Busy").  Query head h reads KV head h / (num_q_heads /
+ * num_kv_heads) (grouped-query attention; the pages do not treat it).
  *
  *   out, q          [num_seqs][num_q_heads][head_dim], contiguous.
  *   num_blocks      blocks in each cache; must be >= 1 when num_seqs > 0
@@ -239,7 +244,9 @@ pa_status pa_decode_static(void* out, const void* q,
  *   seq_lens      [num_chunks] int32, device: keys of chunk c's sequence
  *                 after the chunk, >= n_c.
  *   block_tables  [num_chunks][bt_stride] int32, device.
- *   max_q_len     host bound on n_c (sizes the grid).
+ *   max_q_len     host bound on n_c (sizes the grid).  A chunk with more
+ *                 rows gets NaN in every row the grid covers (at least its
+ *                 first max_q_len rows); rows beyond those are not written.
  *   max_seq_len   host bound on seq_lens (a longer sequence gets NaN rows).
  * ---------------------------------------------------------------------- */
 pa_status pa_prefill_chunk(void* out, const void* q,
