@@ -31,21 +31,16 @@ if not os.path.exists(LIB_PATH):
                       "(python __graft_entry__.py)")
 _lib = ctypes.CDLL(LIB_PATH)
 
-PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_ENOTSUP = range(5)
-PA_POOL_PREFIX_CACHING = 1          # pa_pool_create_ex flag
+from . import _abi
+from ._abi import (PA_EHIP, PA_EINVAL, PA_ENOMEM, PA_ENOTSUP, PA_OK,  # noqa: F401
+                   PA_POOL_PREFIX_CACHING, BlockPool, PAError)
+from ._abi import c_f32, c_i32, c_i64, c_sz, c_vp, P_i32
+
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1      # pa_swap_blocks directions
 PA_FP16, PA_BF16 = 0, 1
 DECODE_STATIC_SCRATCH_BYTES = 16 << 20   # PA_DECODE_STATIC_SCRATCH_BYTES
-_STATUS = {1: "EINVAL", 2: "ENOMEM", 3: "EHIP", 4: "ENOTSUP"}
-
-c_i32, c_i64, c_u64, c_f32, c_sz, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
-                                          ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p)
-P_i32 = ctypes.POINTER(ctypes.c_int32)
-P_i64 = ctypes.POINTER(ctypes.c_int64)
 
 _SIGS = {
-    "pa_last_error": (ctypes.c_char_p, []),
-    "pa_version": (ctypes.c_char_p, []),
     "pa_write_kv": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32,
                             c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
@@ -59,47 +54,17 @@ _SIGS = {
                                  c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
-    "pa_pool_create": (c_i32, [c_i32, c_i32, c_u64, ctypes.POINTER(c_vp)]),
-    "pa_pool_create_ex": (c_i32, [c_i32, c_i32, c_u64, ctypes.c_uint32, c_i32, ctypes.POINTER(c_vp)]),
-    "pa_pool_num_cached": (c_i32, [c_vp]),
-    "pa_pool_num_free_host": (c_i32, [c_vp]),
-    "pa_seq_swap_out": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32]),
-    "pa_seq_swap_in": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32]),
     "pa_swap_blocks": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i32, c_i32, c_i32, c_i32,
                                c_i32, c_i32, c_vp]),
-    "pa_pool_destroy": (None, [c_vp]),
-    "pa_pool_num_free": (c_i32, [c_vp]),
-    "pa_pool_num_blocks": (c_i32, [c_vp]),
-    "pa_block_refcount": (c_i32, [c_vp, c_i32]),
-    "pa_seq_create": (c_i32, [c_vp, P_i64]),
-    "pa_seq_fork": (c_i32, [c_vp, c_i64, P_i64]),
-    "pa_seq_append": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, c_i32, P_i32]),
-    "pa_seq_append_many": (c_i32, [c_vp, P_i64, P_i32, c_i32, P_i64, P_i32, c_i32, P_i32, P_i32]),
-    "pa_seq_fork_many": (c_i32, [c_vp, P_i64, c_i32, P_i64, P_i32]),
-    "pa_seq_free_many": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
-    "pa_seq_append_tokens": (c_i32, [c_vp, c_i64, P_i32, c_i32, c_i32, P_i64, P_i32, c_i32, P_i32,
-                                     P_i32]),
-    "pa_seq_free": (c_i32, [c_vp, c_i64]),
-    "pa_seq_block_table": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i32, P_i32]),
-    "pa_seq_block_tables": (c_i32, [c_vp, P_i64, c_i32, P_i32, c_i32, c_i32, P_i32]),
 }
-for _name, (_res, _args) in _SIGS.items():
-    _f = getattr(_lib, _name)
-    _f.restype = _res
-    _f.argtypes = _args
+_abi.bind(_lib, _abi.HOST_SIGS, default=True)
+_abi.bind(_lib, _SIGS)
 
-EXPORTED = tuple(_SIGS)
-
-
-class PAError(RuntimeError):
-    def __init__(self, status: int, msg: str):
-        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
-        self.status = status
+EXPORTED = tuple(_abi.HOST_SIGS) + tuple(_SIGS)
 
 
 def _check(status: int):
-    if status != PA_OK:
-        raise PAError(status, _lib.pa_last_error().decode())
+    _abi._check(_lib, status)
 
 
 def last_error() -> str:
@@ -120,7 +85,7 @@ def _dtype_code(t) -> int:
         return PA_FP16
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise PAError(PA_ENOTSUP, f"unsupported dtype {t.dtype} (fp16 or bf16)")
 
 
 def _stream(stream=None):
@@ -143,6 +108,38 @@ def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size:
     return (num_blocks, num_kv_heads, block_size // 4, head_dim, 4)
 
 
+def _fail(msg):
+    raise PAError(PA_EINVAL, msg)
+
+
+def _on_device(fn, **tensors):
+    """Every named tensor lives on the GPU (the library takes device pointers)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            _fail(f"{fn}: {name} must be a device (cuda) tensor, got one on {t.device}")
+
+
+def _int_vector(fn, name, t, dtype, n=None):
+    """A contiguous integer vector (or [n, ...] array) of the given dtype."""
+    if t.dtype != dtype:
+        _fail(f"{fn}: {name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        _fail(f"{fn}: {name} must be contiguous")
+    if n is not None and t.shape[0] != n:
+        _fail(f"{fn}: {name} has {t.shape[0]} rows, expected {n}")
+
+
+def _same_16bit(fn, **tensors):
+    """fp16 / bf16 tensors of one dtype, contiguous."""
+    dts = {t.dtype for t in tensors.values()}
+    if len(dts) != 1:
+        _fail(f"{fn}: " + ", ".join(f"{k} is {t.dtype}" for k, t in tensors.items()) + " (one dtype needed)")
+    for name, t in tensors.items():
+        _dtype_code(t)
+        if not t.is_contiguous():
+            _fail(f"{fn}: {name} must be contiguous")
+
+
 def _cache_dims(k_cache, v_cache):
     """(num_blocks, num_kv_heads, block_size, head_dim) of a K/V cache pair."""
     if v_cache.dim() != 5 or v_cache.shape[4] != 4:
@@ -158,10 +155,23 @@ def _cache_dims(k_cache, v_cache):
 
 def write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
     """k, v [T, Hkv, D] (token stride may exceed Hkv*D); slot_mapping int64 [T]."""
+    import torch
+    fn = "write_kv"
     T, H, D = k.shape
-    assert v.shape == k.shape and v.stride() == k.stride()
-    assert k.stride(2) == 1 and k.stride(1) == D
-    N, _, B, _ = _cache_dims(k_cache, v_cache)
+    if v.shape != k.shape or v.stride() != k.stride():
+        _fail(f"{fn}: k and v must have one shape and one stride")
+    if k.stride(2) != 1 or k.stride(1) != D:
+        _fail(f"{fn}: each token's heads must be contiguous ([T, Hkv, D] with a token stride)")
+    if k.dtype != v.dtype:
+        _fail(f"{fn}: k is {k.dtype}, v is {v.dtype}")
+    _same_16bit(fn, k_cache=k_cache, v_cache=v_cache)
+    if k.dtype != k_cache.dtype:
+        _fail(f"{fn}: new tokens are {k.dtype}, the cache is {k_cache.dtype}")
+    _int_vector(fn, "slot_mapping", slot_mapping, torch.int64, T)
+    N, Hc, B, Dc = _cache_dims(k_cache, v_cache)
+    if (Hc, Dc) != (H, D):
+        _fail(f"{fn}: tokens have {H} heads of {D}, the cache {Hc} of {Dc}")
+    _on_device(fn, k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping)
     _check(_lib.pa_write_kv(_ptr(k), _ptr(v), k.stride(0), _ptr(k_cache), _ptr(v_cache),
                             N, _ptr(slot_mapping), T, H, D, B,
                             _dtype_code(k), _stream(stream)))
@@ -169,6 +179,12 @@ def write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None):
     """pairs int32 [n, 2] device tensor of (src, dst)."""
+    import torch
+    _same_16bit("copy_blocks", k_cache=k_cache, v_cache=v_cache)
+    _int_vector("copy_blocks", "pairs", pairs, torch.int32)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        _fail(f"copy_blocks: pairs must be [n, 2], got {tuple(pairs.shape)}")
+    _on_device("copy_blocks", k_cache=k_cache, v_cache=v_cache, pairs=pairs)
     N, H, B, D = _cache_dims(k_cache, v_cache)
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), N, _ptr(pairs), pairs.shape[0],
                                H, D, B, _dtype_code(k_cache), _stream(stream)))
@@ -178,8 +194,15 @@ def swap_blocks(k_cache, v_cache, host_k, host_v, pairs, direction, stream=None)
     """Whole-block copies between the device caches and pinned host tensors of
     the same layout (pin_memory=True).  pairs int32 [n, 2] device tensor:
     (device, host) for PA_SWAP_OUT, (host, device) for PA_SWAP_IN."""
+    import torch
+    _same_16bit("swap_blocks", k_cache=k_cache, v_cache=v_cache, host_k=host_k, host_v=host_v)
+    _int_vector("swap_blocks", "pairs", pairs, torch.int32)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        _fail(f"swap_blocks: pairs must be [n, 2], got {tuple(pairs.shape)}")
     N, H, B, D = _cache_dims(k_cache, v_cache)
-    _cache_dims(host_k, host_v)
+    if _cache_dims(host_k, host_v)[1:] != (H, B, D):
+        _fail("swap_blocks: host and device caches differ in heads, block size or head_dim")
+    _on_device("swap_blocks", k_cache=k_cache, v_cache=v_cache, pairs=pairs)
     if not (host_k.is_pinned() and host_v.is_pinned()):
         raise PAError(PA_EINVAL, "swap_blocks: host tensors must be pinned")
     _check(_lib.pa_swap_blocks(_ptr(k_cache), _ptr(v_cache), N, host_k.data_ptr(), host_v.data_ptr(),
@@ -213,12 +236,34 @@ def decode_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, 
     return int(part.value), int(merge.value), int(waves.value)
 
 
+def _check_decode(fn, out, q, k_cache, v_cache, block_tables, context_lens):
+    """Shapes, dtypes and placement of a decode call; returns (S, Hq, D)."""
+    import torch
+    _same_16bit(fn, out=out, q=q, k_cache=k_cache, v_cache=v_cache)
+    if q.dim() != 3 or out.shape != q.shape:
+        _fail(f"{fn}: q and out must both be [S, Hq, D], got {tuple(q.shape)} and {tuple(out.shape)}")
+    S, Hq, D = q.shape
+    _int_vector(fn, "context_lens", context_lens, torch.int32, S)
+    _int_vector(fn, "block_tables", block_tables, torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] < S:
+        _fail(f"{fn}: block_tables must be [>= {S}, stride], got {tuple(block_tables.shape)}")
+    if _cache_dims(k_cache, v_cache)[3] != D:
+        _fail(f"{fn}: q has head_dim {D}, the cache {_cache_dims(k_cache, v_cache)[3]}")
+    _on_device(fn, out=out, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               context_lens=context_lens)
+    return S, Hq, D
+
+
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
            partition_size=0, workspace=None, stream=None):
     """q/out [S, Hq, D]; block_tables int32 [S, stride]; context_lens int32 [S].
     ``workspace``: uint8 device tensor of decode_workspace_size() bytes."""
     import torch
-    S, Hq, D = q.shape
+    S, Hq, D = _check_decode("decode", out, q, k_cache, v_cache, block_tables, context_lens)
+    if workspace is not None:
+        _on_device("decode", workspace=workspace)
+        if not workspace.is_contiguous():
+            _fail("decode: workspace must be contiguous")
     N, Hkv, B, _ = _cache_dims(k_cache, v_cache)
     need = decode_workspace_size(S, Hq, D, max_context_len, partition_size, Hkv)
     if need and workspace is None:
@@ -236,7 +281,7 @@ def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, max_cont
     """decode() without a workspace: two-pass partition states go to the
     library's static per-device scratch (PA_DECODE_STATIC_SCRATCH_BYTES);
     nothing is allocated.  Calls that overlap on one device race."""
-    S, Hq, D = q.shape
+    S, Hq, D = _check_decode("decode_static", out, q, k_cache, v_cache, block_tables, context_lens)
     N, Hkv, B, _ = _cache_dims(k_cache, v_cache)
     _check(_lib.pa_decode_static(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
@@ -248,160 +293,25 @@ def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, max_cont
 def prefill_chunk(out, q, k_cache, v_cache, block_tables, q_start_loc, seq_lens, max_q_len,
                   max_seq_len, scale, stream=None):
     """q/out [T, Hq, D] packed; q_start_loc int32 [n+1]; seq_lens int32 [n]."""
+    import torch
+    fn = "prefill_chunk"
+    _same_16bit(fn, out=out, q=q, k_cache=k_cache, v_cache=v_cache)
+    if q.dim() != 3 or out.shape != q.shape:
+        _fail(f"{fn}: q and out must both be [T, Hq, D], got {tuple(q.shape)} and {tuple(out.shape)}")
     T, Hq, D = q.shape
-    N, Hkv, B, _ = _cache_dims(k_cache, v_cache)
+    n = seq_lens.shape[0]
+    _int_vector(fn, "seq_lens", seq_lens, torch.int32)
+    _int_vector(fn, "q_start_loc", q_start_loc, torch.int32, n + 1)
+    _int_vector(fn, "block_tables", block_tables, torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] < n:
+        _fail(f"{fn}: block_tables must be [>= {n}, stride], got {tuple(block_tables.shape)}")
+    N, Hkv, B, Dc = _cache_dims(k_cache, v_cache)
+    if Dc != D:
+        _fail(f"{fn}: q has head_dim {D}, the cache {Dc}")
+    _on_device(fn, out=out, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               q_start_loc=q_start_loc, seq_lens=seq_lens)
     _check(_lib.pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
                                  _ptr(block_tables), block_tables.shape[1], _ptr(q_start_loc),
                                  _ptr(seq_lens), seq_lens.shape[0], max_q_len, max_seq_len, Hq,
                                  Hkv, D, B, scale, _dtype_code(q), _stream(stream)))
     return out
-
-
-# ---------------------------------------------------------------------------
-# host block pool
-# ---------------------------------------------------------------------------
-
-class BlockPool:
-    """Refcounted block pool with copy-on-write (host side, ids only)."""
-
-    def __init__(self, num_blocks: int, block_size: int = 16, seed: int = 0,
-                 prefix_caching: bool = False, num_host_blocks: int = 0):
-        h = c_vp()
-        flags = PA_POOL_PREFIX_CACHING if prefix_caching else 0
-        _check(_lib.pa_pool_create_ex(num_blocks, block_size, seed, flags, num_host_blocks,
-                                      ctypes.byref(h)))
-        self._h = h
-        self.block_size = block_size
-
-    def close(self):
-        # At interpreter exit the module globals may already be gone.
-        if getattr(self, "_h", None) and _lib is not None:
-            _lib.pa_pool_destroy(self._h)
-            self._h = None
-
-    def __del__(self):
-        self.close()
-
-    @property
-    def num_free(self) -> int:
-        return int(_lib.pa_pool_num_free(self._h))
-
-    @property
-    def num_blocks(self) -> int:
-        return int(_lib.pa_pool_num_blocks(self._h))
-
-    @property
-    def num_cached(self) -> int:
-        return int(_lib.pa_pool_num_cached(self._h))
-
-    @property
-    def num_free_host(self) -> int:
-        return int(_lib.pa_pool_num_free_host(self._h))
-
-    def _swap(self, fn, seq: int):
-        nb, nt = c_i32(), c_i32()
-        cap = self.num_blocks + 1
-        buf = (c_i32 * (2 * cap))()
-        n = c_i32(0)
-        _check(fn(self._h, seq, buf, cap, ctypes.byref(n)))
-        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
-
-    def swap_out(self, seq: int):
-        """[(device block, host block)] in table order."""
-        return self._swap(_lib.pa_seq_swap_out, seq)
-
-    def swap_in(self, seq: int):
-        """[(host block, device block)] in table order."""
-        return self._swap(_lib.pa_seq_swap_in, seq)
-
-    def refcount(self, block: int) -> int:
-        return int(_lib.pa_block_refcount(self._h, block))
-
-    def create(self) -> int:
-        sid = c_i64()
-        _check(_lib.pa_seq_create(self._h, ctypes.byref(sid)))
-        return sid.value
-
-    def fork(self, parent: int) -> int:
-        sid = c_i64()
-        _check(_lib.pa_seq_fork(self._h, parent, ctypes.byref(sid)))
-        return sid.value
-
-    def append(self, seq: int, n_tokens: int):
-        """Returns (slots: list[int], cow: list[(src, dst)])."""
-        slots = (c_i64 * max(n_tokens, 1))()
-        cow = (c_i32 * 2)()
-        n_cow = c_i32(0)
-        _check(_lib.pa_seq_append(self._h, seq, n_tokens, slots, cow, 1, ctypes.byref(n_cow)))
-        return list(slots[:n_tokens]), ([(cow[0], cow[1])] if n_cow.value else [])
-
-    def fork_many(self, parents):
-        """Forks each parent in order; returns the children's ids."""
-        import numpy as np
-        ids = np.ascontiguousarray(parents, dtype=np.int64)
-        out = np.empty(max(len(ids), 1), dtype=np.int64)
-        done = c_i32(0)
-        _check(_lib.pa_seq_fork_many(self._h, ids.ctypes.data_as(P_i64), len(ids), out.ctypes.data_as(P_i64),
-                                     ctypes.byref(done)))
-        return out[:len(ids)].tolist()
-
-    def free_many(self, seqs):
-        import numpy as np
-        ids = np.ascontiguousarray(seqs, dtype=np.int64)
-        done = c_i32(0)
-        _check(_lib.pa_seq_free_many(self._h, ids.ctypes.data_as(P_i64), len(ids), ctypes.byref(done)))
-
-    def append_many(self, seqs, n_tokens):
-        """Appends n_tokens[i] tokens to seqs[i], in order, in one call.
-        Returns (slots int64 numpy array, cow pairs list).  On failure raises
-        PAError with .n_done = the sequences already applied."""
-        import numpy as np
-        ids = np.ascontiguousarray(seqs, dtype=np.int64)
-        cnt = np.ascontiguousarray(n_tokens, dtype=np.int32)
-        n = len(ids)
-        slots = np.empty(max(int(cnt.clip(min=0).sum()), 1), dtype=np.int64)
-        cow = np.empty((max(n, 1), 2), dtype=np.int32)
-        n_cow, n_done = c_i32(0), c_i32(0)
-        st_ = _lib.pa_seq_append_many(self._h, ids.ctypes.data_as(P_i64), cnt.ctypes.data_as(P_i32), n,
-                                      slots.ctypes.data_as(P_i64), cow.ctypes.data_as(P_i32), max(n, 1),
-                                      ctypes.byref(n_cow), ctypes.byref(n_done))
-        if st_ != PA_OK:
-            err = PAError(st_, last_error())
-            err.n_done = n_done.value
-            raise err
-        return slots[:int(cnt.clip(min=0).sum())], [tuple(x) for x in cow[:n_cow.value].tolist()]
-
-    def append_tokens(self, seq: int, tokens, max_hit_tokens: int):
-        """Returns (slots, cow, n_hit); the first n_hit tokens reuse cached
-        blocks and have slot -1."""
-        n = len(tokens)
-        ids = (c_i32 * max(n, 1))(*[int(t) for t in tokens])
-        slots = (c_i64 * max(n, 1))()
-        cow = (c_i32 * 2)()
-        n_cow, n_hit = c_i32(0), c_i32(0)
-        _check(_lib.pa_seq_append_tokens(self._h, seq, ids, n, max_hit_tokens, slots, cow, 1,
-                                         ctypes.byref(n_cow), ctypes.byref(n_hit)))
-        return list(slots[:n]), ([(cow[0], cow[1])] if n_cow.value else []), n_hit.value
-
-    def free(self, seq: int):
-        _check(_lib.pa_seq_free(self._h, seq))
-
-    def block_table(self, seq: int):
-        nb, nt = c_i32(), c_i32()
-        _check(_lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(nt)))
-        buf = (c_i32 * max(nb.value, 1))()
-        _check(_lib.pa_seq_block_table(self._h, seq, buf, nb.value, ctypes.byref(nb),
-                                       ctypes.byref(nt)))
-        return list(buf[:nb.value]), nt.value
-
-    def block_tables(self, seqs, stride: int, pad: int = 0):
-        """int32 numpy [len(seqs), stride] block tables and int32 context lengths."""
-        import numpy as np
-        n = len(seqs)
-        ids = np.asarray(seqs, dtype=np.int64)
-        out = np.empty((n, stride), dtype=np.int32)
-        ctx = np.empty(n, dtype=np.int32)
-        _check(_lib.pa_seq_block_tables(self._h, ids.ctypes.data_as(P_i64), n,
-                                        out.ctypes.data_as(P_i32), stride, pad,
-                                        ctx.ctypes.data_as(P_i32)))
-        return out, ctx
