@@ -47,6 +47,19 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_16BIT_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
 METRIC = "paged-decode KV GB/s (% of HBM peak) + \u00b5s/step, batch 64 LLaMA-7B shape"
+# Every other workload names its own shape in its metric; only the 7B batch
+# carries the headline metric.
+WORKLOAD_METRIC = {
+    "llama7b": METRIC,
+    "llama8b_gqa": "paged-decode KV GB/s (% of HBM peak) + \u00b5s/step, batch 256 Llama-3.1-8B GQA shape",
+    "llama13b_shared": "paged-decode KV GB/s (% of HBM peak on unique bytes) + \u00b5s/step, batch 128 "
+                       "LLaMA-13B shape with shared prompt prefixes",
+    "mixed": "mixed-step decode KV GB/s (% of HBM peak) + \u00b5s/step, 8192-token chunked-prefill + decode "
+             "step, Llama-3.1-8B GQA shape",
+    "tiny": "paged-decode KV GB/s + \u00b5s/step, 4 sequences, 4 heads, head_dim 64 (latency-bound)",
+    "prefill": "chunked-prefill TFLOP/s (% of MFMA peak) + \u00b5s/step, 2 chunks of 2048 rows over 1024 cached "
+               "tokens, Llama-3.1-8B GQA shape",
+}
 FLUSH_BYTES = 512 << 20
 DECODE_SOURCES = ("paged_kv_cache_422_amd/csrc/decode.hip", "paged_kv_cache_422_amd/csrc/common.hpp",
                   "paged_kv_cache_422_amd/csrc/launch.hpp", "paged_kv_cache_422_amd/csrc/capi.cpp")
@@ -183,6 +196,53 @@ def median(xs):
     return s[len(s) // 2] if s else 0.0
 
 
+def percentile(xs, q):
+    """Nearest-rank percentile (q in 0..100) of a list of step times."""
+    s = sorted(xs)
+    if not s:
+        return 0.0
+    k = max(0, min(len(s) - 1, math.ceil(q / 100 * len(s)) - 1))
+    return s[k]
+
+
+def step_stats(total_ms):
+    """Mean, median, p10 and p90 of per-step times, in us."""
+    return {"us_per_step": round(mean(total_ms) * 1e3, 2), "us_per_step_median": round(median(total_ms) * 1e3, 2),
+            "us_per_step_p10": round(percentile(total_ms, 10) * 1e3, 2),
+            "us_per_step_p90": round(percentile(total_ms, 90) * 1e3, 2)}
+
+
+def host_info():
+    """The host the oracle runs on: cores this process may use, CPU model,
+    and numpy's BLAS library and its thread count."""
+    info = {"host_cores": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [b for b in threadpool_info() if b.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = {"library": blas[0].get("internal_api"), "version": blas[0].get("version"),
+                            "threads": blas[0].get("num_threads")}
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return info
+
+
+def cpu_baseline_line(value, unit, threads, sample, **extra):
+    line = {"value": value, "unit": unit, "cores": threads, "threads_used": threads, "kind": "oracle",
+            "sample": sample}
+    line.update(host_info())
+    line.update(extra)
+    return line
+
+
 def bits(t):
     import numpy as np
     import torch
@@ -223,6 +283,42 @@ def cpu_oracle_decode(q, kc, vc, block_tables, context_lens, scale, dtype, budge
     cpu = time.process_time() - c0
     threads = max(1, round(cpu / spent)) if spent > 0 else 1
     return bytes_done / spent / 1e9, done, spent, threads
+
+
+def cpu_oracle_mixed(w, kc, vc, q_dec, q_pre, n_decode=256, seed=5):
+    """fp64 oracle over the mixed step's work after its write: both prefill
+    chunks in full (every row and head) plus a seeded sample of n_decode
+    decode sequences.  Only the blocks they read are copied back (not
+    timed).  Returns (prefill s, decode s, decode KV bytes, sequences,
+    threads used)."""
+    import numpy as np
+    import torch
+    from oracle import attention as A
+
+    rng = np.random.default_rng(seed)
+    seqs = sorted(rng.choice(w.num_decode, n_decode, replace=False).tolist())
+    need = set()
+    for s_ in seqs:
+        need.update(w.decode_bt[s_, :-(-int(w.decode_lens[s_]) // 16)].tolist())
+    for c in range(w.num_chunks):
+        need.update(w.prefill_bt[c, :-(-int(w.prefill_seq_lens[c]) // 16)].tolist())
+    need = np.array(sorted(need), dtype=np.int64)
+    remap = np.zeros(w.num_blocks, dtype=np.int64)
+    remap[need] = np.arange(len(need))
+    idx = torch.from_numpy(need).to(kc.device)
+    kh, vh = bits(kc[idx]), bits(vc[idx])
+    qd, qp = bits(q_dec), bits(q_pre)
+    pbt = remap[w.prefill_bt].astype(np.int32)
+    dbt = remap[w.decode_bt].astype(np.int32)
+    c0, t0 = time.process_time(), time.perf_counter()
+    A.prefill(qp, kh, vh, pbt, w.q_start_loc, w.prefill_seq_lens, w.scale, w.dtype)
+    t1 = time.perf_counter()
+    A.decode(qd, kh, vh, dbt, w.decode_lens, w.scale, w.dtype, seqs=seqs)
+    t2 = time.perf_counter()
+    cpu = time.process_time() - c0
+    threads = max(1, round(cpu / (t2 - t0))) if t2 > t0 else 1
+    dec_bytes = int(sum(int(w.decode_lens[s_]) for s_ in seqs)) * 2 * w.num_kv_heads * w.head_dim * 2
+    return t1 - t0, t2 - t1, dec_bytes, len(seqs), threads
 
 
 def build_shared_cache(torch, pa, w, k_tok, v_tok):
@@ -321,7 +417,7 @@ def bench_prefix_cache(args, np, torch, pa):
         per, total, wall = timer.run(args.steps, fns)
         flop = sum(prefill_flop(h, n) for h, n in zip(hits, n_new))
         results[caching] = {
-            "us_per_step": round(mean(total) * 1e3, 2), "write_kv_us": round(mean(per[0]) * 1e3, 2),
+            **step_stats(total), "write_kv_us": round(mean(per[0]) * 1e3, 2),
             "prefill_us": round(mean(per[1]) * 1e3, 2), "new_tokens": T, "cached_tokens": sum(hits),
             "prefill_flop": int(flop), "prefill_tflops": round(flop / (mean(per[1]) * 1e-3) / 1e12, 1),
             "host_admit_us_per_request": round(float(np.median(host)), 2), "wall_ms_per_step": round(wall, 5)}
@@ -385,7 +481,7 @@ def bench_swap(args, np, torch, pa):
         timer.run(args.warmup, [fn])
         per, total, wall = timer.run(args.steps, [fn])
         ms = mean(total)
-        res[k] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+        res[k] = {"us": round(ms * 1e3, 1), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2), **step_stats(total)}
     rt_ms = (res["swap_out"]["us"] + res["swap_in"]["us"]) / 1e3
     gbs = round(2 * nbytes / (rt_ms * 1e-3) / 1e9, 2)
     line = {
@@ -519,19 +615,32 @@ def bench_beam(args, np, torch, pa):
     used = N - pool.num_free
     private = sum(-(-pool.block_table(s)[1] // B) for s in seqs)
     kv_bytes = int(sum(pool.block_table(s)[1] for s in seqs)) * 2 * Hkv * D * 2
+    # Each physical block counted once, with the slots its holders use: a
+    # prompt block shared by four beams is read from HBM once, then from cache.
+    filled = {}
+    for sq in seqs:
+        tab, n_tok = pool.block_table(sq)
+        for j, phys in enumerate(tab):
+            filled[phys] = max(filled.get(phys, 0), min(B, n_tok - B * j))
+    unique_bytes = int(sum(filled.values())) * 2 * Hkv * D * 2
+    uniq_gbs = unique_bytes / (mean(dev) * 1e-3) / 1e9
     line = {
         "metric": "beam-search step (width 4): fork / copy-on-write / write / decode, and memory saved by sharing",
         "value": round(mean(dev) * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        **step_stats(dev),
         "ms_per_step": round(mean(dev), 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"beam: {R} requests x {WID} beams, {PROMPT}-token prompts, 32 query heads over 8 KV "
                                "heads, head_dim 128, bf16; step = parent choice, fork/free, one token per beam "
                                "(copy-on-write), block copies + slot-mapped write + decode of all beams",
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (mean(dev) * 1e-3) / 1e9, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kv_bytes / (mean(dev) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "whole device step (block copies + write + decode), logical KV bytes of the last step"},
+        "roofline": {"bound": "hbm", "achieved": round(uniq_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(uniq_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes": "unique physical KV bytes the last step's decode reads (each shared block once), "
+                              "over the whole device step",
+                     "kernel": "whole device step (block copies + write + decode)"},
+        "logical_kv_bytes": kv_bytes, "unique_kv_bytes": unique_bytes,
+        "logical_GBps": round(kv_bytes / (mean(dev) * 1e-3) / 1e9, 2),
         "host_pool_us_per_step": round(float(np.median(host_us)), 1),
         "copy_on_write_pairs_per_step": round(mean(cow_counts), 2),
         "wall_ms_per_step": round(wall, 5),
@@ -587,9 +696,9 @@ def main():
         ms = mean(total)
         tflops = w.prefill_flops / (ms * 1e-3) / 1e12
         line = {
-            "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "metric": WORKLOAD_METRIC["prefill"], "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-            "us_per_step": round(ms * 1e3, 2), "us_per_step_median": round(median(total) * 1e3, 2),
+            **step_stats(total),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
             "data": "synthetic",
             "config": {"workload": f"prefill: {w.num_chunks} chunks of {w.prefill_chunk} query rows over "
@@ -722,17 +831,26 @@ def main():
                                   "frac_mfma": round(tflops / MFMA_16BIT_PEAK_TFLOPS, 4)}
 
     cpu = None
-    if args.cpu_budget > 0:
-        seqs = None
-        if name == "mixed":
-            rng = np.random.default_rng(5)
-            seqs = sorted(rng.choice(num_seqs, 64, replace=False).tolist())
+    if args.cpu_budget > 0 and name == "mixed":
+        print("bench.py: fp64 oracle on both prefill chunks and 256 decode sequences", file=sys.stderr,
+              flush=True)
+        t_pre, t_dec, dec_bytes, n_seq, threads = cpu_oracle_mixed(w, kc, vc, q_dec, q_pre)
+        cpu = cpu_baseline_line(
+            round(dec_bytes / t_dec / 1e9, 6), "GB/s", threads,
+            f"both prefill chunks in full ({w.num_chunks} x {w.prefill_chunk} rows, all {Hq} query heads) in "
+            f"{t_pre:.1f} s, then {n_seq} seeded decode sequences of the {num_seqs} (all {Hq} query heads "
+            f"each) in {t_dec:.1f} s; value = decode KV GB/s of that sample",
+            prefill_s=round(t_pre, 3), decode_sample_s=round(t_dec, 3),
+            step_s_extrapolated=round(t_pre + t_dec * num_seqs / n_seq, 2),
+            extrapolation="prefill time + sample decode time x (decode sequences / sample); the write is a "
+                          "bit copy and not timed")
+    elif args.cpu_budget > 0:
         gbs_cpu, n_seq, wall_cpu, threads = cpu_oracle_decode(
-            q_dec_t, kc_t, vc_t, bt_np, ctx_np, w.scale, w.dtype, args.cpu_budget, seqs)
-        cpu = {"value": round(gbs_cpu, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": f"{n_seq} single-sequence fp64 decodes (all {Hq} query heads each) over "
-                         f"{'a seeded 64-sequence subset' if seqs else f'the {num_seqs} sequences'} "
-                         f"of this workload in order, in {wall_cpu:.1f} s; KV GB/s of the sample"}
+            q_dec_t, kc_t, vc_t, bt_np, ctx_np, w.scale, w.dtype, args.cpu_budget)
+        cpu = cpu_baseline_line(
+            round(gbs_cpu, 6), "GB/s", threads,
+            f"{n_seq} single-sequence fp64 decodes (all {Hq} query heads each) over the {num_seqs} "
+            f"sequences of this workload in order, in {wall_cpu:.1f} s; KV GB/s of the sample")
 
     traffic = profiled_traffic(f"decode_{name}_pmc.md", DECODE_SOURCES)
     # A shared prompt's blocks are read once per sequence that shares them,
@@ -743,15 +861,14 @@ def main():
         roof_gbs = extra["unique_kv_bytes_per_step"] / (dec_ms * 1e-3) / 1e9
         roof_bytes = "unique physical KV bytes (each shared block once)"
     line = {
-        "metric": METRIC,
+        "metric": WORKLOAD_METRIC[name],
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "us_per_step": round(ms * 1e3, 2),
-        "us_per_step_median": round(median(total) * 1e3, 2),
+        **step_stats(total),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -42,3 +42,27 @@ def test_committed_decode_profiles_parse():
         path = os.path.join(ROOT, "profiles", f"decode_{wl}_pmc.md")
         text = open(path).read()
         assert "traffic_bytes_per_launch:" in text and "source_sha256:" in text
+
+
+def test_each_workload_names_its_own_metric():
+    """Only the 7B batch carries the headline metric; every other workload's
+    line says which shape it measured."""
+    names = ["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill"]
+    assert set(bench.WORKLOAD_METRIC) == set(names)
+    assert bench.WORKLOAD_METRIC["llama7b"] == bench.METRIC
+    assert len(set(bench.WORKLOAD_METRIC.values())) == len(names)
+
+
+def test_step_statistics():
+    xs = [0.001 * i for i in range(1, 11)]        # 1 .. 10 us, in ms
+    st = bench.step_stats(xs)
+    assert st["us_per_step"] == 5.5 and st["us_per_step_p10"] == 1.0 and st["us_per_step_p90"] == 9.0
+    assert st["us_per_step_median"] == 6.0
+    assert bench.percentile([], 50) == 0.0
+
+
+def test_cpu_baseline_records_the_host():
+    line = bench.cpu_baseline_line(1.5, "GB/s", 3, "sample text")
+    assert line["cores"] == line["threads_used"] == 3 and line["kind"] == "oracle"
+    assert line["host_cores"] == len(os.sched_getaffinity(0))
+    assert "cpu_model" in line and "blas" in line
