@@ -9,9 +9,9 @@ What the pages fix:
     [IV §PagedAttention: What the OS Figured Out Decades Ago];
   * blocks are claimed on demand and released as soon as a sequence finishes
     [IV §PagedAttention ...], [RW §How PagedAttention Works];
-  * sequences branched from one prompt share its blocks through reference
-    counts; only when a branch writes a new token is *that* block copied, the
-    rest stays shared [IV §Copy-on-Write Makes Beam Search Cheap],
+  * branches of one prompt hold its blocks by reference count, and a block
+    is duplicated for a branch only at the moment that branch writes into
+    it; every other block stays common [IV §Copy-on-Write Makes Beam Search Cheap],
     [RW §How PagedAttention Works], [TG §How PagedAttention Reclaims GPU
     Memory];
   * the allocator acts as the page-frame table of the pool [IV §Python LLM

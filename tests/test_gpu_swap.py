@@ -43,8 +43,8 @@ def test_swap_blocks_bit_exact_both_ways(dtype, H, D):
 
 def test_swap_blocks_rejects_unpinned_host_memory():
     kc = torch.zeros(pa.k_cache_shape(4, 1, 64), dtype=torch.float16, device=DEV)
-    vc = torch.zeros(4, 1, 64, 16, dtype=torch.float16, device=DEV)
-    host = np.zeros((4, 1, 16, 64), dtype=np.float16)          # ordinary pageable memory
+    vc = torch.zeros(pa.v_cache_shape(4, 1, 64), dtype=torch.float16, device=DEV)
+    host = np.zeros((4, 1, 2, 16, 32), dtype=np.float16)       # ordinary pageable memory, one block per K tile
     pairs = torch.tensor([[0, 0]], dtype=torch.int32, device=DEV)
     st_ = pa._lib.pa_swap_blocks(kc.data_ptr(), vc.data_ptr(), 4, host.ctypes.data, host.ctypes.data, 4,
                                  pairs.data_ptr(), 1, pa.PA_SWAP_OUT, 1, 64, 16, pa.PA_FP16, None)

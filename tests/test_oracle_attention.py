@@ -284,9 +284,9 @@ def test_softmax_rows_sum_to_one_and_unit_values_give_unit_output():
 
 
 def test_block_permutation_invariance():
-    """'Non-contiguous physical blocks appear contiguous from the attention
-    kernel's perspective' (Inside vLLM, section 'PagedAttention: What the OS
-    Figured Out Decades Ago'): relabelling physical blocks changes nothing."""
+    """Attention reads a sequence's scattered blocks as one run of tokens
+    (Inside vLLM, section "PagedAttention: What the OS Figured Out Decades
+    Ago"), so relabelling the physical blocks changes nothing."""
     rng = np.random.default_rng(10)
     lens = [40, 1, 64, 17]
     kc, vc, bt = paged_layout(rng, lens, 2, 32, "bf16", extra=5)

@@ -78,12 +78,13 @@ class DecodeWorkload:
             self.num_kv_heads * self.head_dim * 2
 
     def cache_shapes(self):
-        """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, D, B] (dim-major)."""
+        """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, B/4, D, 4]
+        (groups of four slots, dim-major within a group)."""
         N, H, B, D = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
         return (N, H, D // 32, B, 32), (N, H, B // 4, D, 4)
 
     def make_tensors(self, device="cpu", seed_offset=0):
-        """q [S, Hq, D], k_cache [N, Hkv, D/32, B, 32], v_cache [N, Hkv, D, B]."""
+        """q [S, Hq, D], k_cache [N, Hkv, D/32, B, 32], v_cache [N, Hkv, B/4, D, 4]."""
         import torch
         g = torch.Generator(device=device)
         g.manual_seed(self.seed + seed_offset)
@@ -266,7 +267,8 @@ class MixedWorkload:
         return self.num_new_tokens * 2 * self.num_kv_heads * self.head_dim * 2 * 2
 
     def cache_shapes(self):
-        """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, D, B] (dim-major)."""
+        """K [N, Hkv, D/32, B, 32] (32-dim chunks) and V [N, Hkv, B/4, D, 4]
+        (groups of four slots, dim-major within a group)."""
         N, H, B, D = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
         return (N, H, D // 32, B, 32), (N, H, B // 4, D, 4)
 
