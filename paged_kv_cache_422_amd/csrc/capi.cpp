@@ -45,11 +45,13 @@ pa_status hip_result(const char* fn, hipError_t e) {
   return ok();
 }
 
-// Virtual waves of a decode partition (the interleave that fixes the
-// reduction order, see the decode kernels): 8 for partitions of 128 blocks or
-// more, else 4.  A function of the partition size alone, so a sequence's
-// result depends only on its own data and the partition size.
-int32_t decode_virtual_waves(int32_t part_blocks) { return part_blocks >= 128 ? 8 : 4; }
+// Waves that interleave the blocks of one decode partition (which fixes the
+// reduction order): 8 for partitions of 128 blocks or more (a long partition
+// then finishes about as fast as a 64-block one with 4 waves, which keeps the
+// end of the launch short), else 4.  A function of the partition size alone,
+// so a sequence's result depends only on its own data and the partition
+// size.
+int32_t decode_waves(int32_t part_blocks) { return part_blocks >= 128 ? 8 : 4; }
 
 // Whether pa_decode merges a sequence's partitions on chip, in one pass, and
 // with how many wave groups per workgroup (0: two passes through the
@@ -221,9 +223,7 @@ void fill_decode_plan(pa::DecodeArgs& a, int32_t num_seqs, int32_t num_q_heads, 
   a.part_blocks = P / kBlock;
   a.max_parts = static_cast<int32_t>(std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P));
   a.max_context_len = max_context_len;
-  a.waves = decode_virtual_waves(a.part_blocks);
-  a.launch_waves = a.waves;
-  a.pair_blocks = 0;
+  a.waves = decode_waves(a.part_blocks);
   a.fuse_groups = decode_fuse_groups(static_cast<int64_t>(num_seqs) * num_kv_heads * num_sub, group,
                                      max_context_len);
 }

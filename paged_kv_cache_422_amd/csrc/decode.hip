@@ -248,7 +248,7 @@ __device__ __forceinline__ void merge_partitions(const float* ml, const float* a
   for (int i = 0; i < PER; ++i) out_row[lane + 64 * i] = from_f32<T>(o[i] / lsum);
 }
 
-// Per-wave softmax states of NS segments (a segment is one virtual wave of
+// Per-wave softmax states of NS segments (a segment is one wave's share of
 // one partition): running max (log2 units), running sum and unnormalised
 // accumulator, for each of NH query heads.
 template <int NH, int D, int NS>
@@ -258,21 +258,21 @@ struct WaveStates {
   float o[NS][NH][D];
 };
 
-// The blocks of a partition are interleaved over VW virtual waves: virtual
-// wave v takes blocks start + v, start + v + VW, ... and keeps its own
-// softmax state, and the partition's state is the merge of its VW virtual
-// states in index order (merge_waves).  VW depends only on the partition
-// size, so it fixes the reduction order.  A workgroup runs a partition on pw
-// physical waves: physical wave wl runs virtual waves wl, wl + pw, ... one
-// after another, its register pipeline running on across the switch.  How
-// many physical waves a partition gets is therefore a free choice that
-// never changes a bit of the result.
+// The blocks of a partition are interleaved over VW waves: wave v takes
+// blocks start + v, start + v + VW, ... and keeps its own softmax state, and
+// the partition's state is the merge of its VW wave states in index order
+// (merge_waves).  VW depends only on the partition size, so it fixes the
+// reduction order.  (The walk below also lets pw < VW physical waves run the
+// VW interleaved states, each taking several in turn, with results unchanged
+// bit for bit; measured on MI355X, 4 physical waves for 8 states beat 8 only
+// on batches of short contexts and lost elsewhere, so the kernels run one
+// physical wave per state.)
 //
-// A cursor is a position in the list of (partition p, virtual wave v,
+// A cursor is a position in the list of (partition p, wave state v,
 // absolute block j) a physical wave visits: partitions p_first, p_first +
 // p_step, ... below p_end (partition p holds blocks [pstart(p), pstart(p +
-// 1))), virtual waves wl, wl + pw, ... below VW, blocks in steps of VW.  Its
-// state goes to segment slot p * VW + v.  p >= p_end once the wave is done.
+// 1))), states wl, wl + pw, ... below VW, blocks in steps of VW.  Its state
+// goes to segment slot p * VW + v.  p >= p_end once the wave is done.
 struct Cursor {
   int p, v, j;
 };
@@ -449,29 +449,25 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[D / 32], const uint16_t* q_ro
   }
 }
 
-// One partition of one (sequence, head group) per item.  W physical waves
-// per workgroup run the partition's VW virtual waves.  With PAIR, a
-// partition of fewer than pair_blocks blocks is short enough that W / 2
-// waves suffice: the workgroup of an even head group then also takes the
-// next head group of the same sequence and partition, waves 0 .. W/2-1 on
-// one and W/2 .. W-1 on the other, and the odd head group's workgroup exits
-// at once.  The choice depends only on the partition's own length and does
-// not change the result (see SegmentWalk).  Two register pipelines of three
-// buffers each fit two waves per SIMD.
-template <class T, int D, int NH, int W, int VW, bool PAIR>
+// One partition of one (sequence, head group) per workgroup of W waves
+// (W = 4 or 8, the partition's interleave).  Three register buffers per wave
+// fit two waves per SIMD.
+template <class T, int D, int NH, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * W;
-  constexpr int NITEM = PAIR ? 2 : 1;
-  static_assert(VW % W == 0 || (PAIR && VW % (W / 2) == 0), "virtual waves must split evenly");
-  __shared__ WaveStates<NH, D, VW> st[NITEM];
+  __shared__ WaveStates<NH, D, W> st;
 
   // blockIdx.x = (part * num_seqs + s) * (num_kv_heads * num_sub) + head group
   const int n_hg = a.num_kv_heads * a.num_sub;
-  const int hg0 = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_hg));
+  const int hg = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_hg));
   const uint32_t rest = blockIdx.x / static_cast<uint32_t>(n_hg);
   const int s = static_cast<int>(rest % static_cast<uint32_t>(a.num_seqs));
   const int part = static_cast<int>(rest / static_cast<uint32_t>(a.num_seqs));
+  const int g = hg / a.num_sub;
+  const int sub = hg - g * a.num_sub;
+  const int hq0 = g * a.group + sub * 16;
+  const int nh = min(16, a.group - sub * 16);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -481,9 +477,6 @@ void decode_partition_kernel(DecodeArgs a) {
   if (np <= 0) {
     // Empty context: zero rows.  Invalid length: NaN rows.  Partition 0 only.
     if (part == 0) {
-      const int g = hg0 / a.num_sub;
-      const int hq0 = g * a.group + (hg0 - g * a.num_sub) * 16;
-      const int nh = min(16, a.group - (hg0 - g * a.num_sub) * 16);
       const uint16_t fill = np == 0 ? uint16_t(0) : from_f32<T>(NAN);
       for (int i = tid; i < nh * D; i += kThreads)
         a.out[(static_cast<int64_t>(s) * a.num_q_heads + hq0 + i / D) * D + i % D] = fill;
@@ -496,49 +489,30 @@ void decode_partition_kernel(DecodeArgs a) {
   const int blk0 = partition_start(part, nb_seq, np);
   const int nblk = partition_start(part + 1, nb_seq, np) - blk0;   // 1 .. part_blocks
 
-  const bool paired = PAIR && nblk < a.pair_blocks;
-  if (paired && (hg0 & 1)) return;            // taken by the even neighbour's workgroup
-  const int item = paired ? static_cast<int>(w >= W / 2) : 0;
-  const int pw = paired ? W / 2 : W;
-  const int wl = w - item * (W / 2) * static_cast<int>(paired);
-  const int hg = hg0 + item;
-  const bool active = hg < n_hg;              // an odd last head group leaves a half idle
-  const int g = hg / a.num_sub;
-  const int sub = hg - g * a.num_sub;
-  const int hq0 = g * a.group + sub * 16;
-  const int nh = min(16, a.group - sub * 16);
-
   int bt[kBtRegs];
   bool bad_id;
   load_table(bt, a.block_tables + static_cast<int64_t>(s) * a.bt_stride + blk0, nblk, lane, a.num_blocks,
              bad_id);
   const bool poison = __any(bad_id);
 
-  WaveStates<NH, D, VW>& my = st[item];
-  if (active) {
-    for (int v = wl; v < VW; v += pw)
-      if (v >= nblk) store_empty(my, v, lane);
-    u32x4 qb[D / 32];
-    load_q<D>(qb, a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0) * D, nh, lane);
-    const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
-    const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
-    const int hl = lane & 15, quad = lane >> 4;
-    const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
-    const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
-    auto pstart = [=](int p) { return blk0 + (p > 0 ? nblk : 0); };
-    const SegmentWalk<VW, decltype(pstart)> walk{1, 1, wl, pw, pstart};
-    run_wave<T, D, NH, VW, VW>(walk, 0, bt, blk0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, my);
-  }
+  if (w >= nblk) store_empty(st, w, lane);
+  u32x4 qb[D / 32];
+  load_q<D>(qb, a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0) * D, nh, lane);
+  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
+  const int hl = lane & 15, quad = lane >> 4;
+  const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
+  const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
+  auto pstart = [=](int p) { return blk0 + (p > 0 ? nblk : 0); };
+  const SegmentWalk<W, decltype(pstart)> walk{1, 1, w, W, pstart};
+  run_wave<T, D, NH, W, W>(walk, 0, bt, blk0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
   __syncthreads();
 
-  if (!active) return;
-  const int t0 = paired ? tid - item * (kThreads / 2) : tid;
-  const int tn = paired ? kThreads / 2 : kThreads;
-  for (int i = t0; i < nh * D; i += tn) {
+  for (int i = tid; i < nh * D; i += kThreads) {
     const int h = i / D;
     const int d = i - h * D;
     float M, lsum, acc;
-    merge_waves<VW, NH, D>(my.m, my.l, my.o, h, d, M, lsum, acc);
+    merge_waves<W, NH, D>(st.m, st.l, st.o, h, d, M, lsum, acc);
     if (poison) acc = NAN;
     const int64_t row = static_cast<int64_t>(s) * a.num_q_heads + hq0 + h;
     if (np == 1) {
@@ -557,8 +531,8 @@ void decode_partition_kernel(DecodeArgs a) {
 // Single-pass split-KV: one workgroup of NGRP * W waves takes every
 // partition of one (sequence, head group) and merges them on chip, so the
 // partition states never go through HBM.  Wave group gi = w / W takes
-// partitions gi, gi + NGRP, ...; inside a partition its W waves run the VW
-// virtual waves exactly as decode_partition_kernel does, each segment's state
+// partitions gi, gi + NGRP, ...; inside a partition its W waves interleave
+// the blocks exactly as decode_partition_kernel does, each segment's state
 // goes to LDS, and the states are merged with the same code as the two-pass
 // path (merge_waves, then merge_partitions).  The result is therefore
 // bit-identical to decode_partition_kernel + decode_merge_kernel at the same
@@ -576,12 +550,12 @@ constexpr int fused_max_parts() {
   return budget / per_part < 32 ? budget / per_part : 32;
 }
 
-template <class T, int D, int NH, int W, int NGRP, int VW>
+template <class T, int D, int NH, int W, int NGRP>
 __global__ __launch_bounds__(64 * W * NGRP) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_fused_kernel(DecodeArgs a) {
+  constexpr int VW = W;
   constexpr int kThreads = 64 * W * NGRP;
   constexpr int PMAX = fused_max_parts<VW, NH, D, kThreads>();
-  static_assert(VW % W == 0, "virtual waves must split evenly");
   __shared__ WaveStates<NH, D, PMAX * VW> st;
   __shared__ float sm_ml[NH][PMAX][2];
 
@@ -632,8 +606,8 @@ void decode_fused_kernel(DecodeArgs a) {
   run_wave<T, D, NH, PMAX * VW, VW>(walk, gi, bt, 0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
   __syncthreads();
 
-  // Per partition, the VW virtual-wave states merged (same code as the
-  // two-pass kernel).  A partition's accumulator replaces its first state in
+  // Per partition, the VW wave states merged (same code as the two-pass
+  // kernel).  A partition's accumulator replaces its first state in
   // place: the element (p * VW, h, d) is read only by the thread that writes it.
   for (int i = tid; i < np * nh * D; i += kThreads) {
     const int p = i / (nh * D);
@@ -694,40 +668,26 @@ int merge_kind_nh(const DecodeArgs& a) {
   }
 }
 
-template <class T, int D, int NH, int W, int VW, bool PAIR>
-void launch_partition(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, W, VW, PAIR>), dim3(static_cast<uint32_t>(n_wg)),
-                     dim3(64 * W), 0, stream, a);
-}
-
 template <class T, int D, int NH>
 hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
   if constexpr (NH <= 8) {
     if (merge_kind_nh<D, NH>(a) == kMergeOnChip) {
-      // One workgroup per (sequence, KV head): 8 waves on the 8 virtual waves
-      // of long partitions, or two groups of 4 waves taking alternate short
-      // partitions.
+      // One workgroup per (sequence, KV head): 8 waves on long partitions, or
+      // two groups of 4 waves taking alternate short partitions.
       const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.num_kv_heads));
       if (a.waves == 8)
-        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, 8, 1, 8>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, 8, 1>), grid, dim3(512), 0, stream, a);
       else
-        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, 4, 2, 4>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((decode_fused_kernel<T, D, NH, 4, 2>), grid, dim3(512), 0, stream, a);
       return hipGetLastError();
     }
   }
-  if (a.waves == 4) {
-    launch_partition<T, D, NH, 4, 4, false>(a, stream);
-  } else if (a.launch_waves == 4) {
-    launch_partition<T, D, NH, 4, 8, false>(a, stream);
-  } else if (a.pair_blocks > 0) {
-    if constexpr (NH <= 4)
-      launch_partition<T, D, NH, 8, 8, true>(a, stream);
-    else
-      launch_partition<T, D, NH, 8, 8, false>(a, stream);
-  } else {
-    launch_partition<T, D, NH, 8, 8, false>(a, stream);
-  }
+  const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
+  if (a.waves == 8)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 8>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 4>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;

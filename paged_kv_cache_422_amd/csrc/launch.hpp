@@ -54,9 +54,7 @@ struct DecodeArgs {
   int32_t part_blocks;        // partition size in blocks
   int32_t max_parts;
   int32_t max_context_len;
-  int32_t waves;              // virtual waves interleaving a partition's blocks (4 or 8): the reduction order
-  int32_t launch_waves;       // physical waves per workgroup of the two-pass kernel (speed only)
-  int32_t pair_blocks;        // > 0: a partition of fewer blocks runs on half the waves, two head groups per workgroup
+  int32_t waves;              // waves interleaving a partition's blocks (4 or 8): fixes the reduction order
   int32_t fuse_groups;        // > 0: single pass, partitions merged on chip by this many wave groups
   float scale_log2;           // scale * log2(e)
 };
