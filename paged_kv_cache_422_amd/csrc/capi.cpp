@@ -53,6 +53,20 @@ pa_status hip_result(const char* fn, hipError_t e) {
 // size.
 int32_t decode_waves(int32_t part_blocks) { return part_blocks >= 128 ? 8 : 4; }
 
+// Block buffers per wave of the partition kernel with 8 waves: two (one
+// block in flight during the work on another) when no context can exceed
+// 2048 tokens, else three.  Short contexts give each wave only a few blocks,
+// and a deeper pipeline then spends more of them filling and draining; long
+// ones want the bytes in flight.  Measured on MI355X, same box, alternating
+// builds: two buffers took the 13B shared-prefix batch (2048-token cap,
+// median 400) from 257-258 to 247-249 us with the 7B batch unchanged
+// (193.5-193.9 against 193.8-194.1 us), but slowed the mixed step's decode
+// (contexts up to 4096 tokens) by up to 6%.  The buffer count changes no
+// result bit.
+int32_t decode_buffers(int32_t waves, int32_t max_context_len) {
+  return waves == 8 && max_context_len <= 2048 ? 2 : 3;
+}
+
 // Whether pa_decode merges a sequence's partitions on chip, in one pass, and
 // with how many wave groups per workgroup (0: two passes through the
 // workspace).  One pass needs a batch that fills the GPU without splitting
@@ -224,6 +238,7 @@ void fill_decode_plan(pa::DecodeArgs& a, int32_t num_seqs, int32_t num_q_heads, 
   a.max_parts = static_cast<int32_t>(std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P));
   a.max_context_len = max_context_len;
   a.waves = decode_waves(a.part_blocks);
+  a.buffers = decode_buffers(a.waves, max_context_len);
   a.fuse_groups = decode_fuse_groups(static_cast<int64_t>(num_seqs) * num_kv_heads * num_sub, group,
                                      max_context_len);
 }

@@ -337,12 +337,12 @@ __device__ __forceinline__ int64_t table_entry(const int (&bt)[kBtRegs], int jj)
 }
 
 // Everything one physical wave does for one (sequence, head group): walk its
-// segments with a three-buffer register pipeline (the loads of the next two
-// blocks are in flight while it works on the current one) and leave the
-// state of every segment it visits in st.  Segments it has no block in must
-// hold the empty state beforehand (store_empty).  `tbl_base` is the absolute
+// segments with a register pipeline of NBUF block buffers (the loads of the
+// next NBUF - 1 blocks are in flight while it works on the current one) and
+// leave the state of every segment it visits in st.  Segments it has no block
+// in must hold the empty state beforehand (store_empty).  `tbl_base` is the absolute
 // block index of table register lane 0.
-template <class T, int D, int NH, int NS, int VW, class Walk>
+template <class T, int D, int NH, int NS, int VW, int NBUF, class Walk>
 __device__ __forceinline__ void run_wave(const Walk& walk, int p_first, const int (&bt)[kBtRegs], int tbl_base,
                                          int L, const u32x4 (&qb)[D / 32], float scale_log2,
                                          const uint16_t* kbase, const uint16_t* vbase, int64_t blk_elems,
@@ -396,29 +396,50 @@ __device__ __forceinline__ void run_wave(const Walk& walk, int p_first, const in
   if (c0.p >= walk.p_end) return;
   Cursor c1 = c0;
   walk.advance(c1);
-  Cursor c2 = c1;
-  walk.advance(c2);
-  BlockRegs<T, D> b0, b1, b2;
-  load_block<T, D>(b0, kbase, vbase, off(c0.j));
-  load_block<T, D>(b1, kbase, vbase, pf_off(c1));
-  auto shift = [&]() {
-    c0 = c1;
-    c1 = c2;
+  if constexpr (NBUF == 2) {
+    // One block in flight while the wave works on another.
+    BlockRegs<T, D> b0, b1;
+    load_block<T, D>(b0, kbase, vbase, off(c0.j));
+    auto shift = [&]() {
+      c0 = c1;
+      walk.advance(c1);
+    };
+    for (;;) {
+      load_block<T, D>(b1, kbase, vbase, pf_off(c1));
+      process(b0, c0);
+      shift();
+      if (c0.p >= walk.p_end) break;
+      load_block<T, D>(b0, kbase, vbase, pf_off(c1));
+      process(b1, c0);
+      shift();
+      if (c0.p >= walk.p_end) break;
+    }
+  } else {
+    // Two blocks in flight while the wave works on a third.
+    Cursor c2 = c1;
     walk.advance(c2);
-  };
-  for (;;) {
-    load_block<T, D>(b2, kbase, vbase, pf_off(c2));
-    process(b0, c0);
-    shift();
-    if (c0.p >= walk.p_end) break;
-    load_block<T, D>(b0, kbase, vbase, pf_off(c2));
-    process(b1, c0);
-    shift();
-    if (c0.p >= walk.p_end) break;
-    load_block<T, D>(b1, kbase, vbase, pf_off(c2));
-    process(b2, c0);
-    shift();
-    if (c0.p >= walk.p_end) break;
+    BlockRegs<T, D> b0, b1, b2;
+    load_block<T, D>(b0, kbase, vbase, off(c0.j));
+    load_block<T, D>(b1, kbase, vbase, pf_off(c1));
+    auto shift = [&]() {
+      c0 = c1;
+      c1 = c2;
+      walk.advance(c2);
+    };
+    for (;;) {
+      load_block<T, D>(b2, kbase, vbase, pf_off(c2));
+      process(b0, c0);
+      shift();
+      if (c0.p >= walk.p_end) break;
+      load_block<T, D>(b0, kbase, vbase, pf_off(c2));
+      process(b1, c0);
+      shift();
+      if (c0.p >= walk.p_end) break;
+      load_block<T, D>(b1, kbase, vbase, pf_off(c2));
+      process(b2, c0);
+      shift();
+      if (c0.p >= walk.p_end) break;
+    }
   }
   flush();
 }
@@ -450,9 +471,9 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[D / 32], const uint16_t* q_ro
 }
 
 // One partition of one (sequence, head group) per workgroup of W waves
-// (W = 4 or 8, the partition's interleave).  Three register buffers per wave
-// fit two waves per SIMD.
-template <class T, int D, int NH, int W>
+// (W = 4 or 8, the partition's interleave), each with NBUF block buffers
+// (2 or 3; either fits two waves per SIMD).
+template <class T, int D, int NH, int W, int NBUF>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * W;
@@ -505,7 +526,7 @@ void decode_partition_kernel(DecodeArgs a) {
   const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
   auto pstart = [=](int p) { return blk0 + (p > 0 ? nblk : 0); };
   const SegmentWalk<W, decltype(pstart)> walk{1, 1, w, W, pstart};
-  run_wave<T, D, NH, W, W>(walk, 0, bt, blk0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
+  run_wave<T, D, NH, W, W, NBUF>(walk, 0, bt, blk0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
   __syncthreads();
 
   for (int i = tid; i < nh * D; i += kThreads) {
@@ -603,7 +624,7 @@ void decode_fused_kernel(DecodeArgs a) {
   const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
   const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
   const SegmentWalk<VW, decltype(pstart)> walk{NGRP, np, wl, W, pstart};
-  run_wave<T, D, NH, PMAX * VW, VW>(walk, gi, bt, 0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
+  run_wave<T, D, NH, PMAX * VW, VW, 3>(walk, gi, bt, 0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
   __syncthreads();
 
   // Per partition, the VW wave states merged (same code as the two-pass
@@ -684,10 +705,12 @@ hipError_t launch_nh(const DecodeArgs& a, hipStream_t stream) {
   }
   const int64_t n_wg = static_cast<int64_t>(a.max_parts) * a.num_seqs * a.num_kv_heads * a.num_sub;
   const dim3 grid(static_cast<uint32_t>(n_wg));
-  if (a.waves == 8)
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 8>), grid, dim3(512), 0, stream, a);
+  if (a.waves == 8 && a.buffers == 2)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 8, 2>), grid, dim3(512), 0, stream, a);
+  else if (a.waves == 8)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 8, 3>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, NH, 4, 3>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;

@@ -55,6 +55,7 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t max_context_len;
   int32_t waves;              // waves interleaving a partition's blocks (4 or 8): fixes the reduction order
+  int32_t buffers;            // block buffers per wave of the two-pass kernel (2 or 3): speed only
   int32_t fuse_groups;        // > 0: single pass, partitions merged on chip by this many wave groups
   float scale_log2;           // scale * log2(e)
 };

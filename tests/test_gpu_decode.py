@@ -185,6 +185,24 @@ def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_le
     assert np.array_equal(bad[keep], f[keep])
 
 
+def test_pipeline_depth_changes_no_bit():
+    """A batch of >= 1024 (sequence, KV head) items with contexts of at most
+    2048 tokens runs 8 waves with two block buffers when max_context_len is
+    2048 and three when it is larger; every sequence still has one partition,
+    so the two calls must agree bit for bit (and match the oracle)."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(1, 2049, 96).tolist() + [2048, 1, 16, 17]
+    q, kc, vc, bt, ctx = small_case(len(lens), 32, 32, 128, torch.float16, lens, seed=17)
+    print(f"pipeline depth: {len(lens)} sequences", flush=True)
+    for mc in (2048, 2064):
+        part, merge, waves = pa.decode_plan(len(lens), 32, 32, 128, mc, 0)
+        assert merge == pa.MERGE_NONE and waves == 8, (mc, part, merge, waves)
+    two = run_decode(q, kc, vc, bt, ctx, 2048, 1 / math.sqrt(128))
+    three = run_decode(q, kc, vc, bt, ctx, 2064, 1 / math.sqrt(128))
+    assert torch.equal(two.view(torch.int16), three.view(torch.int16))
+    assert_close(two, oracle_decode(q, kc, vc, bt, ctx, 1 / math.sqrt(128)), what="two buffers")
+
+
 def test_partition_size_changes_only_rounding():
     lens = [2000, 1500, 999]
     q, kc, vc, bt, ctx = small_case(3, 8, 8, 128, torch.float16, lens, seed=14)
