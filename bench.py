@@ -57,6 +57,8 @@ WORKLOAD_METRIC = {
     "mixed": "mixed-step decode KV GB/s (% of HBM peak) + \u00b5s/step, 8192-token chunked-prefill + decode "
              "step, Llama-3.1-8B GQA shape",
     "tiny": "paged-decode KV GB/s + \u00b5s/step, 4 sequences, 4 heads, head_dim 64 (latency-bound)",
+    "llama8b_long": "paged-decode KV GB/s (% of HBM peak) + \u00b5s/step, 32 sequences of 8192-32768 tokens, "
+                    "Llama-3.1-8B GQA shape",
     "prefill": "chunked-prefill TFLOP/s (% of MFMA peak) + \u00b5s/step, 2 chunks of 2048 rows over 1024 cached "
                "tokens, Llama-3.1-8B GQA shape",
 }
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill",
-                             "prefix_cache", "swap", "beam"])
+                             "prefix_cache", "swap", "beam", "llama8b_long"])
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's own, 0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,

@@ -47,7 +47,7 @@ def test_committed_decode_profiles_parse():
 def test_each_workload_names_its_own_metric():
     """Only the 7B batch carries the headline metric; every other workload's
     line says which shape it measured."""
-    names = ["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill"]
+    names = ["llama7b", "llama8b_gqa", "llama13b_shared", "mixed", "tiny", "prefill", "llama8b_long"]
     assert set(bench.WORKLOAD_METRIC) == set(names)
     assert bench.WORKLOAD_METRIC["llama7b"] == bench.METRIC
     assert len(set(bench.WORKLOAD_METRIC.values())) == len(names)

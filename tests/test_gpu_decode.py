@@ -10,7 +10,7 @@ import torch
 import paged_kv_cache_422_amd as pa
 from oracle import attention as A
 from tests.gpu_util import DEV, assert_close, bits, dtype_name, run_decode, set_v_slots
-from workloads import llama7b, llama8b_gqa, tiny
+from workloads import llama7b, llama8b_gqa, llama8b_long, tiny
 
 pytestmark = pytest.mark.gpu
 
@@ -219,6 +219,35 @@ def test_long_partitions_use_every_table_register():
     want = oracle_decode(q, kc, vc, bt, ctx, 0.088)
     for P in (4096, 2048, 1040):
         assert_close(run_decode(q, kc, vc, bt, ctx, 4096, 0.088, P), want, what=f"P={P}")
+
+
+def test_contexts_longer_than_one_partition_table():
+    """Contexts above 4096 tokens (one partition's block table) are split
+    into partitions whose states the second pass merges: the library's own
+    partitioning and caller sizes of 512 and 4096 tokens."""
+    lens = [12000, 4097, 8191, 300, 9000]
+    S, Hq, Hkv, D = len(lens), 8, 2, 128
+    q, kc, vc, bt, ctx = small_case(S, Hq, Hkv, D, torch.bfloat16, lens, seed=16)
+    want = oracle_decode(q, kc, vc, bt, ctx, 0.088)
+    for P in (0, 512, 4096):
+        part, merge, _ = pa.decode_plan(S, Hq, Hkv, D, 12000, P)
+        assert merge == pa.MERGE_TWO_PASS and part <= 4096, (P, part, merge)
+        assert_close(run_decode(q, kc, vc, bt, ctx, 12000, 0.088, P), want, what=f"P={P}")
+
+
+def test_long_context_workload_sampled():
+    """The long-context benchmark workload at full size (32 sequences of
+    8k-32k tokens), library partitioning, eight seeded sequences checked
+    against the oracle."""
+    w = llama8b_long()
+    print(f"{w.name}: S={w.num_seqs} blocks={w.num_blocks}", flush=True)
+    q, kc, vc = w.make_tensors(DEV)
+    out = run_decode(q, kc, vc, w.block_tables, w.context_lens, w.max_model_len, w.scale)
+    seqs = sorted(np.random.default_rng(17).choice(w.num_seqs, 8, replace=False).tolist())
+    want = A.decode(bits(q), bits(kc), bits(vc), w.block_tables, w.context_lens, w.scale, w.dtype,
+                    seqs=seqs)
+    r = assert_close(out[seqs], want[seqs], what=w.name)
+    print(f"  worst err/bound {r:.3f}", flush=True)
 
 
 @pytest.mark.parametrize("make", [llama7b, llama8b_gqa], ids=["llama7b", "llama8b_gqa"])

@@ -1,7 +1,7 @@
 """The seeded generators are deterministic and draw the stated shapes."""
 import numpy as np
 
-from workloads import llama7b, llama8b_gqa, llama13b_shared, mixed, tiny
+from workloads import llama7b, llama8b_gqa, llama8b_long, llama13b_shared, mixed, tiny
 
 
 def _valid_layout(w):
@@ -40,6 +40,14 @@ def test_llama8b_gqa():
     assert (w.num_q_heads, w.num_kv_heads, w.dtype, w.partition_size) == (32, 8, "bf16", 512)
     assert w.context_lens.min() >= 512 and w.context_lens.max() <= 4096
     assert w.block_tables.shape == (256, 256)
+    _valid_layout(w)
+
+
+def test_llama8b_long():
+    w = llama8b_long()
+    assert (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.dtype, w.partition_size) == (32, 32, 8, "bf16", 0)
+    assert w.context_lens.min() >= 8192 and w.context_lens.max() <= 32768
+    assert w.block_tables.shape == (32, 2048) and w.max_model_len == 32768
     _valid_layout(w)
 
 

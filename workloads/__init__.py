@@ -22,8 +22,12 @@ lengths and values of those models' attention shapes stand in for them):
   mixed         one step of 8192 tokens at the 8B GQA shape: 4096 decode
                 tokens (L ~ U[256, 4096]) + 2 prefill chunks of 2048 query
                 tokens over 1024 cached tokens each.
+  llama8b_long  32 sequences at the 8B GQA shape, bf16, L ~ U[8192, 32768]:
+                contexts longer than one partition's block table (4096
+                tokens), library partitioning.
 
-Seeds: workload i (1..5 in the order above) uses seed 4220 + i.  Host-side
+Seeds: workload i (1..5 in the order above) uses seed 4220 + i; llama8b_long
+uses 4226.  Host-side
 metadata comes from numpy's PCG64; tensors come from a torch.Generator on the
 device they are created on.
 """
@@ -31,6 +35,6 @@ from __future__ import annotations
 
 from .configs import (  # noqa: F401
     DecodeWorkload, MixedWorkload, SharedWorkload, WORKLOADS,
-    make_workload, tiny, llama7b, llama13b_shared, llama8b_gqa, mixed,
+    make_workload, tiny, llama7b, llama13b_shared, llama8b_gqa, llama8b_long, mixed,
     normal_tensor, torch_dtype,
 )

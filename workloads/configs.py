@@ -119,6 +119,17 @@ def llama8b_gqa(seed: int = 4224, num_seqs: int = 256) -> DecodeWorkload:
                           partition_size=512, max_model_len=4096)
 
 
+def llama8b_long(seed: int = 4226, num_seqs: int = 32) -> DecodeWorkload:
+    """Long contexts, 8192 to 32768 tokens: each is longer than one
+    partition's block table (4096 tokens), so every sequence is split into
+    partitions whose states the second pass merges."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(8192, 32768 + 1, size=num_seqs).astype(np.int32)
+    bt, n, pad = _scatter_layout(lens, BLOCK_SIZE, 2048, rng)
+    return DecodeWorkload("llama8b_long", seed, 32, 8, 128, "bf16", lens, bt, n, pad,
+                          max_model_len=32768)
+
+
 # ---------------------------------------------------------------------------
 # prefix sharing (copy-on-write) workload: logical description only.  The
 # physical layout is produced by whoever lays it out (the block pool, or a
@@ -317,6 +328,7 @@ WORKLOADS = {
     "llama7b": llama7b,
     "llama13b_shared": llama13b_shared,
     "llama8b_gqa": llama8b_gqa,
+    "llama8b_long": llama8b_long,
     "mixed": mixed,
 }
 
