@@ -65,6 +65,23 @@ def test_prefill_shapes(dtype, Hq, Hkv, D):
     assert_close(out, want, what=f"prefill Hq={Hq} Hkv={Hkv} D={D}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [(4, 2, 128, torch.bfloat16), (16, 8, 64, torch.float16),
+                                            (16, 2, 128, torch.float16), (32, 2, 64, torch.bfloat16),
+                                            (32, 1, 128, torch.bfloat16)],
+                         ids=["g2", "g2-D64", "g8", "g16-D64", "g32"])
+def test_prefill_group_sizes(Hq, Hkv, D, dtype):
+    """Query-head groups of 2, 8, 16 and 32 per KV head: a workgroup then
+    covers 2 heads x 4 row tiles or 4 heads x 2 row tiles, and a KV group
+    spans several workgroups."""
+    chunks = [(0, 3), (31, 70), (200, 129), (7, 33)]
+    print(f"prefill groups Hq={Hq} Hkv={Hkv} D={D} {dtype}", flush=True)
+    q, kc, vc, bt, qsl, lens = prefill_case(chunks, Hq, Hkv, D, dtype, seed=Hq * 7 + D)
+    scale = 1 / math.sqrt(D)
+    out = run_prefill(q, kc, vc, bt, qsl, lens, scale)
+    want = A.prefill(bits(q), bits(kc), bits(vc), bt, qsl, lens, scale, dtype_name(q))
+    assert_close(out, want, what=f"prefill Hq={Hq} Hkv={Hkv} D={D}")
+
+
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_prefill_long_context(dtype):
     """Cached context past 1024 blocks (16384 keys), so tiles take block ids
