@@ -172,6 +172,10 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
  *                   bytes for the same arguments (may be NULL if that size is
  *                   0; the single pass leaves it untouched); contents need not
  *                   be initialised.
+ * Launch limits (PA_ENOTSUP beyond them): num_seqs <= 65535, and each grid's
+ * work-item count below 2^32 (partitions x num_seqs x head groups of up to 16
+ * query heads x 64 x waves for the partition kernel, num_seqs x num_q_heads x
+ * 64 for the merge kernel).
  * ---------------------------------------------------------------------- */
 int32_t   pa_default_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_context_len);
@@ -248,6 +252,8 @@ pa_status pa_decode_static(void* out, const void* q,
  *                 rows gets NaN in every row the grid covers (at least its
  *                 first max_q_len rows); rows beyond those are not written.
  *   max_seq_len   host bound on seq_lens (a longer sequence gets NaN rows).
+ * Launch limits (PA_ENOTSUP beyond them): num_chunks <= 65535 and
+ * ceil(max_q_len / 64) * 512 < 2^32 (about 5.4e8 rows).
  * ---------------------------------------------------------------------- */
 pa_status pa_prefill_chunk(void* out, const void* q,
                            const void* k_cache, const void* v_cache, int64_t num_blocks,

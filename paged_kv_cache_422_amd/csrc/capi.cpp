@@ -67,15 +67,16 @@ int32_t decode_buffers(int32_t waves, int32_t max_context_len) {
   return waves == 8 && max_context_len <= 2048 ? 2 : 3;
 }
 
-// Whether pa_decode merges a sequence's partitions on chip, in one pass, and
-// with how many wave groups per workgroup (0: two passes through the
-// workspace).  One pass needs a batch that fills the GPU without splitting
-// (so one workgroup per sequence and head group is enough work), contexts
-// whose block table fits the kernel's registers (4096 tokens) and head
-// groups of at most 8 query heads; the kernel also checks that the
-// partitions fit its LDS.  Two groups of 4 waves per workgroup measured
-// faster than one (8B-GQA shape at 512-token partitions: 403 against 418
-// us; two passes took 458).  Either way the result is the same, bit for bit.
+// Whether pa_decode may merge a sequence's partitions on chip, in one pass
+// (nonzero), or goes through the workspace in two passes (0).  One pass needs
+// a batch that fills the GPU without splitting (so one workgroup per sequence
+// and head group is enough work), contexts whose block table fits the
+// kernel's registers (4096 tokens) and head groups of at most 8 query heads;
+// the kernel also checks that the partitions fit its LDS.  Its workgroup is
+// one group of 8 waves for partitions of 128 blocks or more and two groups of
+// 4 waves taking alternate partitions below: two groups of 4 measured faster
+// than one (8B-GQA shape at 512-token partitions: 403 against 418 us; two
+// passes took 458).  Either way the result is the same, bit for bit.
 int32_t decode_fuse_groups(int64_t items, int32_t group, int32_t max_context_len) {
   if (group > 8 || max_context_len > kMaxPartitionTokens) return 0;
   return items >= kTargetItems ? 2 : 0;
@@ -313,12 +314,14 @@ pa_status decode_call(const char* fn, void* out, const void* q, const void* k_ca
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t num_sub = (group + 15) / 16;
   const int64_t max_parts = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + P - 1) / P);
-  // One workgroup of 256 work-items per (partition, sequence, head group);
-  // the launch's work-item count must fit the dispatch packet's 32 bits.
-  if (max_parts * num_seqs * num_kv_heads * num_sub * 256 > static_cast<int64_t>(UINT32_MAX))
-    return fail(PA_ENOTSUP, f + ": too many (partition, sequence, head) work items");
   pa::DecodeArgs a{};
   fill_decode_plan(a, num_seqs, num_q_heads, num_kv_heads, P, max_context_len);
+  // One workgroup of 64 * waves work-items per (partition, sequence, head
+  // group), and one wave per (sequence, query head) in the merge pass; each
+  // launch's work-item count must fit the dispatch packet's 32 bits.
+  if (max_parts * num_seqs * num_kv_heads * num_sub * 64 * a.waves > static_cast<int64_t>(UINT32_MAX) ||
+      static_cast<int64_t>(num_seqs) * num_q_heads * 64 > static_cast<int64_t>(UINT32_MAX))
+    return fail(PA_ENOTSUP, f + ": too many (partition, sequence, head) work items");
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * max_parts;
   size_t need = 0;
   if (from_scratch) {
@@ -395,6 +398,10 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(PA_EINVAL, "pa_prefill_chunk: num_q_heads must be a positive multiple of num_kv_heads");
   if (num_chunks == 0 || max_q_len == 0) return ok();
+  // Row blocks of at least 64 rows, one 512-work-item workgroup each: the
+  // grid's first dimension must fit the dispatch packet's 32 bits.
+  if ((static_cast<int64_t>(max_q_len) + 63) / 64 * 512 > static_cast<int64_t>(UINT32_MAX))
+    return fail(PA_ENOTSUP, "pa_prefill_chunk: max_q_len too large for one launch");
   // A bad block id reads block 0 (its tile is then discarded).
   if (num_blocks == 0)
     return fail(PA_EINVAL, "pa_prefill_chunk: num_blocks must be positive when there are chunks");

@@ -14,10 +14,12 @@
 // is cut into np = ceil(nb / part_blocks) partitions of nearly equal size
 // (partition p covers blocks [p*nb/np, (p+1)*nb/np)), so every work item of a
 // sequence is within one block of the others and long sequences do not leave
-// a short remainder item for the end of the launch.  One 256-thread
-// workgroup (4 wave64s) handles one (sequence, KV head, partition) for all
-// query heads of that KV head's group, so K/V are read once per group.  Wave
-// w takes blocks w, w+4, ... of the partition; waves merge through LDS.  A
+// a short remainder item for the end of the launch.  One workgroup of W
+// wave64s handles one (sequence, KV head, partition) for all query heads of
+// that KV head's group, so K/V are read once per group; W is 8 for
+// partitions of 128 blocks or more and 4 below, so it depends only on the
+// partition size.  Wave w takes blocks w, w+W, ... of the partition; waves
+// merge through LDS.  A
 // sequence with one partition writes its output directly; otherwise each
 // partition writes (max, sum, unnormalised accumulator) and a second kernel
 // merges them by log-sum-exp.  When the batch alone fills the GPU, one

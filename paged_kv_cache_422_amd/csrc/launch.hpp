@@ -56,7 +56,7 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t waves;              // waves interleaving a partition's blocks (4 or 8): fixes the reduction order
   int32_t buffers;            // block buffers per wave of the two-pass kernel (2 or 3): speed only
-  int32_t fuse_groups;        // > 0: single pass, partitions merged on chip by this many wave groups
+  int32_t fuse_groups;        // > 0: single pass allowed, partitions merged on chip (wave groups per workgroup: 1 of 8 waves or 2 of 4, by `waves`)
   float scale_log2;           // scale * log2(e)
 };
 

@@ -103,6 +103,29 @@ def test_decode_rejects_small_workspace_and_misalignment():
     assert st_ == pa.PA_ENOTSUP
 
 
+def test_decode_rejects_a_grid_beyond_the_dispatch_limit():
+    # 2048-token partitions run 8-wave (512 work-item) workgroups: 3 x 65535 x 64
+    # of them are 6.4e9 work-items, past the dispatch packet's 32 bits (at 256
+    # work-items per workgroup they would still fit).
+    # No workspace is passed, so without the check the call would still stop
+    # at the workspace test, before any launch.
+    fake = ctypes.c_void_p(0x1000)
+    _, _, waves = pa.decode_plan(65535, 64, 64, 128, 3 * 2048, 2048)
+    assert waves == 8
+    st_ = pa._lib.pa_decode(fake, fake, fake, fake, 100, fake, 384, fake, 65535, 64, 64, 128, 16, 3 * 2048,
+                            0.1, 2048, None, 0, pa.PA_FP16, None)
+    assert st_ == pa.PA_ENOTSUP and "work items" in pa.last_error()
+    # The same grid with one partition fewer fits.
+    st_ = pa._lib.pa_decode(fake, fake, fake, fake, 100, fake, 384, fake, 65535, 64, 64, 128, 16, 2 * 2048,
+                            0.1, 2048, None, 0, pa.PA_FP16, None)
+    assert st_ == pa.PA_EINVAL and "workspace" in pa.last_error()
+    # 16-head groups at 1024-token partitions: the partition kernel's 2 x 65535 x 128
+    # workgroups of 256 fit, the merge pass's 65535 x 2048 waves do not.
+    st_ = pa._lib.pa_decode(fake, fake, fake, fake, 100, fake, 384, fake, 65535, 2048, 128, 128, 16, 2 * 1024,
+                            0.1, 1024, None, 0, pa.PA_FP16, None)
+    assert st_ == pa.PA_ENOTSUP and "work items" in pa.last_error()
+
+
 def test_zero_sized_calls_are_noops():
     assert pa._lib.pa_write_kv(None, None, 0, None, None, 0, None, 0, 8, 128, 16, 0, None) == pa.PA_OK
     assert pa._lib.pa_copy_blocks(None, None, 0, None, 0, 8, 128, 16, 0, None) == pa.PA_OK
@@ -163,6 +186,18 @@ def test_prefill_rejects_before_launch(kw, code):
                                    a["num_chunks"], 64, 1024, a["num_q_heads"], a["num_kv_heads"],
                                    a["head_dim"], a["block_size"], 0.1, pa.PA_BF16, None)
     assert st_ == code, pa.last_error()
+
+
+def test_prefill_rejects_a_grid_beyond_the_dispatch_limit():
+    # 2^30 rows per chunk need 2^24 workgroups of 512 work-items in the grid's
+    # first dimension, past the dispatch packet's 32 bits.  Null pointers: a
+    # call that got past this check would still stop at the pointer test.
+    st_ = pa._lib.pa_prefill_chunk(None, None, None, None, 100, None, 8, None, None, 2, 1 << 30, 1 << 30,
+                                   32, 8, 128, 16, 0.1, pa.PA_BF16, None)
+    assert st_ == pa.PA_ENOTSUP and "max_q_len" in pa.last_error()
+    st_ = pa._lib.pa_prefill_chunk(None, None, None, None, 100, None, 8, None, None, 2, 1 << 20, 1 << 20,
+                                   32, 8, 128, 16, 0.1, pa.PA_BF16, None)
+    assert st_ == pa.PA_EINVAL and "null" in pa.last_error()
 
 
 def test_decode_and_prefill_reject_an_empty_pool_with_work():
