@@ -70,6 +70,9 @@ namespace {
 
 constexpr int kBlock = 16;   // tokens per KV block == MFMA tile edge
 constexpr int kBtRegs = 4;   // block-table registers per lane: partitions up to 256 blocks
+// Partitions of at most this many blocks run the 8 interleaved wave states of
+// the two-buffer partition kernel on 4 waves (see decode_partition_kernel).
+constexpr int kHalfWaveBlocks = 24;
 
 // -1: invalid context length; 0: empty; otherwise number of partitions.
 __device__ __forceinline__ int num_partitions(int L, const DecodeArgs& a) {
@@ -264,11 +267,12 @@ struct WaveStates {
 // blocks start + v, start + v + VW, ... and keeps its own softmax state, and
 // the partition's state is the merge of its VW wave states in index order
 // (merge_waves).  VW depends only on the partition size, so it fixes the
-// reduction order.  (The walk below also lets pw < VW physical waves run the
+// reduction order.  The walk below also lets pw < VW physical waves run the
 // VW interleaved states, each taking several in turn, with results unchanged
-// bit for bit; measured on MI355X, 4 physical waves for 8 states beat 8 only
-// on batches of short contexts and lost elsewhere, so the kernels run one
-// physical wave per state.)
+// bit for bit.  Measured on MI355X, 4 physical waves for 8 states over a
+// whole launch beat 8 only on batches of short contexts and lost elsewhere,
+// so the kernels run one physical wave per state except on short partitions
+// of the two-buffer kernel (decode_partition_kernel).
 //
 // A cursor is a position in the list of (partition p, wave state v,
 // absolute block j) a physical wave visits: partitions p_first, p_first +
@@ -475,8 +479,22 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[D / 32], const uint16_t* q_ro
 // One partition of one (sequence, head group) per workgroup of W waves
 // (W = 4 or 8, the partition's interleave), each with NBUF block buffers
 // (2 or 3; either fits two waves per SIMD).
+//
+// Short partitions on the two-buffer 8-wave kernel (contexts of at most 2048
+// tokens): a workgroup's fixed cost (start-up latency, the merge, the idle
+// ends of its waves) is a large share of a partition of a few blocks per
+// wave.  So a partition of at most kHalfWaveBlocks blocks runs its 8 wave
+// states on waves 0-3 (wave w takes states w and w + 4 in turn, each over
+// the same blocks in the same order, so the result is unchanged bit for
+// bit), and waves 4-7 exit at once.  That kernel is capped at 3 waves per
+// SIMD instead of 2 (140 registers fit 3), so the next workgroup can start
+// beside the 4 remaining waves instead of after them.  Measured on MI355X,
+// same box, three alternating runs: the 13B shared-prefix batch (median 400
+// tokens) 247.7-248.4 -> 237.5-238.9 us, the 7B batch 193.3-194.0 -> 193.1-
+// 193.2 us; cut-offs of 32-48 blocks took the 7B batch up to 197.5 us, 16
+// blocks gained the 13B batch only 242 us.
 template <class T, int D, int NH, int W, int NBUF>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, NBUF == 2 ? 3 : 2)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * W;
   __shared__ WaveStates<NH, D, W> st;
@@ -511,6 +529,10 @@ void decode_partition_kernel(DecodeArgs a) {
   const int nb_seq = (L + kBlock - 1) / kBlock;
   const int blk0 = partition_start(part, nb_seq, np);
   const int nblk = partition_start(part + 1, nb_seq, np) - blk0;   // 1 .. part_blocks
+  // Physical waves running the W wave states.  Whole waves leave before any
+  // barrier; the barrier below then waits only for the waves that remain.
+  const int pw = (W == 8 && NBUF == 2 && nblk <= kHalfWaveBlocks) ? W / 2 : W;
+  if (w >= pw) return;
 
   int bt[kBtRegs];
   bool bad_id;
@@ -518,7 +540,8 @@ void decode_partition_kernel(DecodeArgs a) {
              bad_id);
   const bool poison = __any(bad_id);
 
-  if (w >= nblk) store_empty(st, w, lane);
+  for (int v = w; v < W; v += pw)
+    if (v >= nblk) store_empty(st, v, lane);
   u32x4 qb[D / 32];
   load_q<D>(qb, a.q + (static_cast<int64_t>(s) * a.num_q_heads + hq0) * D, nh, lane);
   const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
@@ -527,11 +550,11 @@ void decode_partition_kernel(DecodeArgs a) {
   const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
   const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
   auto pstart = [=](int p) { return blk0 + (p > 0 ? nblk : 0); };
-  const SegmentWalk<W, decltype(pstart)> walk{1, 1, w, W, pstart};
+  const SegmentWalk<W, decltype(pstart)> walk{1, 1, w, pw, pstart};
   run_wave<T, D, NH, W, W, NBUF>(walk, 0, bt, blk0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
   __syncthreads();
 
-  for (int i = tid; i < nh * D; i += kThreads) {
+  for (int i = tid; i < nh * D; i += 64 * pw) {
     const int h = i / D;
     const int d = i - h * D;
     float M, lsum, acc;

@@ -185,17 +185,21 @@ def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_le
     assert np.array_equal(bad[keep], f[keep])
 
 
-def test_pipeline_depth_changes_no_bit():
+@pytest.mark.parametrize("hq,hkv,dtype,max_len", [(32, 32, torch.float16, 2048), (32, 8, torch.bfloat16, 640)])
+def test_pipeline_depth_changes_no_bit(hq, hkv, dtype, max_len):
     """A batch of >= 1024 (sequence, KV head) items with contexts of at most
     2048 tokens runs 8 waves with two block buffers when max_context_len is
     2048 and three when it is larger; every sequence still has one partition,
-    so the two calls must agree bit for bit (and match the oracle)."""
+    so the two calls must agree bit for bit (and match the oracle).  With two
+    buffers a partition of at most 24 blocks runs its 8 wave states on 4
+    waves, so the lengths straddle that cut-off (384 tokens)."""
     rng = np.random.default_rng(17)
-    lens = rng.integers(1, 2049, 96).tolist() + [2048, 1, 16, 17]
-    q, kc, vc, bt, ctx = small_case(len(lens), 32, 32, 128, torch.float16, lens, seed=17)
-    print(f"pipeline depth: {len(lens)} sequences", flush=True)
+    n = 1024 // hkv
+    lens = rng.integers(1, max_len + 1, n - 9).tolist() + [2048, 1, 16, 17, 368, 369, 384, 385, 400]
+    q, kc, vc, bt, ctx = small_case(len(lens), hq, hkv, 128, dtype, lens, seed=17)
+    print(f"pipeline depth: {len(lens)} sequences, {hq}/{hkv} heads, {dtype}", flush=True)
     for mc in (2048, 2064):
-        part, merge, waves = pa.decode_plan(len(lens), 32, 32, 128, mc, 0)
+        part, merge, waves = pa.decode_plan(len(lens), hq, hkv, 128, mc, 0)
         assert merge == pa.MERGE_NONE and waves == 8, (mc, part, merge, waves)
     two = run_decode(q, kc, vc, bt, ctx, 2048, 1 / math.sqrt(128))
     three = run_decode(q, kc, vc, bt, ctx, 2064, 1 / math.sqrt(128))
