@@ -29,8 +29,9 @@
 // it is staged (exact up to 65504: bf16's 8 significant bits fit in fp16's
 // 11) and P.V runs in fp16 with one product per weight.  bf16 weights alone
 // (8 significant bits) would break the tolerance when a few keys carry the
-// softmax, so a workgroup that meets a V value beyond fp16's range starts
-// over with bf16 weights split into hi + lo halves (two products).
+// softmax, so a workgroup whose fp16 pass read a V value beyond fp16's range
+// (it converts to inf, and the accumulators end non-finite) starts over with
+// bf16 weights split into hi + lo halves (two products).
 //
 // Operand layouts.  In LDS the K rows of each 32-key half are stored with
 // bits 2 and 3 of the key index swapped, so the accumulator element i of
@@ -67,11 +68,12 @@ struct PrefillLds {
   static constexpr int kBytesK = kTileKeys * kRow;
   static constexpr int kBytesVBlock = D * kVRow;
   static constexpr int kBytesStage = kBytesK + kTileBlocks * kBytesVBlock;
-  static constexpr int kBytes = kBytesStage + 16;  // + the wide flag
+  static constexpr int kBytes = kBytesStage;
 };
 
 template <class X> struct TypeTag { using type = X; };
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Position of key r (0..31) of a 32-key half in LDS: bits 2 and 3 swapped.
 __device__ __forceinline__ int swap_bits23(int r) {
@@ -228,11 +230,12 @@ void prefill_kernel(PrefillArgs a) {
   };
   // Registers -> LDS.  V slots past the sequence end are zeroed (they may
   // hold stale data, and 0 * NaN would leak into P.V).  With kHalf the V
-  // tile is stored as fp16: bf16 -> fp16 is exact for magnitudes up to 65504
-  // (8 significant bits fit in 11) and loses at most 2^-24 in absolute terms
-  // below fp16's normal range; a larger or non-finite value sets `wide`.
-  auto stash = [&](auto half_tag, const u32x4 (&pk)[UPT], const u32x4 (&pv)[UPT], int t,
-                   bool& wide) __attribute__((always_inline)) {
+  // tile is stored as fp16, rounded to nearest: bf16 -> fp16 is exact for
+  // magnitudes up to 65504 (8 significant bits fit in 11) and loses at most
+  // 2^-25 in absolute terms below fp16's normal range; every larger bf16
+  // magnitude (65536 and up) becomes inf, and NaN stays NaN.
+  auto stash = [&](auto half_tag, const u32x4 (&pk)[UPT], const u32x4 (&pv)[UPT],
+                   int t) __attribute__((always_inline)) {
     constexpr bool kHalf = decltype(half_tag)::value;
 #pragma unroll
     for (int r = 0; r < UPT; ++r) {
@@ -273,29 +276,18 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
       if constexpr (kHalf) {
-        // Largest magnitude of each 16-bit half, one packed integer max per dword.
-        u16x2 mag = {0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t x = v[e];
-          mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, x & 0x7fff7fffu));
-          const auto h2 = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, x << 16),
-                                                     __builtin_bit_cast(float, x & 0xffff0000u));
-          v[e] = __builtin_bit_cast(uint32_t, h2);
+          const f32x2 f = {__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xffff0000u)};
+          v[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
         }
-        wide |= max(mag[0], mag[1]) > 0x477f;   // bf16 bits of 65280, the largest below 65504
       }
       unsigned char* const vrow = lds + Lds::kBytesK + b * Lds::kBytesVBlock + d0 * Lds::kVRow + kg * 8;
       *reinterpret_cast<u32x2*>(vrow) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(vrow + Lds::kVRow) = u32x2{v[2], v[3]};
     }
   };
-
-  // Set by any wave whose stash met a V value beyond fp16's range, read by
-  // every wave after the barrier that publishes the tile.  Thread 0 clears it
-  // before the first barrier of the pass; it is only ever set afterwards.
-  int* const wide_flag = reinterpret_cast<int*>(lds + Lds::kBytesStage);
-  if (tid == 0) *wide_flag = 0;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[DT];
@@ -444,51 +436,45 @@ void prefill_kernel(PrefillArgs a) {
   // bottom (an odd count gets one more, fully masked tile whose compute
   // returns at once): a break between the two halves would merge a path on
   // which set 1 was never loaded into the loop header and force every wait
-  // there to drain all loads; for the same reason the pass gives up only at
-  // the bottom.  With kHalf (bf16 data, V as fp16) a wave whose stash met a
-  // wide value sets the flag before the barrier that publishes the tile, and
-  // the flag is read once per pair, after the second such barrier.  It is
-  // never cleared during the pass and no wave can set it again before every
-  // wave has passed the next barrier, so all waves read the same value and
-  // leave together; tiles computed from an unusable fp16 copy meanwhile are
-  // discarded with the pass.
-  auto run = [&](auto half_tag) __attribute__((always_inline)) -> bool {
-    constexpr bool kHalf = decltype(half_tag)::value;
+  // there to drain all loads.
+  auto run = [&](auto half_tag) __attribute__((always_inline)) {
     fetch(pk0, pv0, 0);
     __builtin_amdgcn_sched_barrier(0);   // keep set 0's loads older than set 1's
     fetch(pk1, pv1, 1);
     int t = 0;
     do {
-      bool wide = false;
       __syncthreads();                 // every wave is done with the previous tile
-      stash(half_tag, pk0, pv0, t, wide);
-      if constexpr (kHalf) {
-        if (wide) *wide_flag = 1;
-      }
+      stash(half_tag, pk0, pv0, t);
       __syncthreads();                 // tile t is in LDS
       preload_k();
       fetch(pk0, pv0, t + 2);
       compute(half_tag, t);
       __syncthreads();
-      stash(half_tag, pk1, pv1, t + 1, wide);
-      if constexpr (kHalf) {
-        if (wide) *wide_flag = 1;
-      }
+      stash(half_tag, pk1, pv1, t + 1);
       __syncthreads();
-      const int gave_up = kHalf ? __builtin_amdgcn_readfirstlane(*wide_flag) : 0;
       preload_k();
       fetch(pk1, pv1, t + 3);
       compute(half_tag, t + 1);
-      if (gave_up) return false;
       t += 2;
     } while (t < n_tiles);
-    return true;
   };
-  // bf16 data first tries the fp16 P.V (one product per weight); a workgroup
-  // that meets a V value beyond fp16's range starts over with split bf16
-  // weights (two products per weight).
+  // bf16 data first tries the fp16 P.V (one product per weight).  A V value
+  // the fp16 copy could not hold (inf, NaN, or 65536 and up) makes the
+  // accumulators of every wave that read its tile non-finite: its weight is
+  // finite and >= 0, and 0 * inf is NaN in the matrix product.  A workgroup
+  // where any accumulator ended non-finite starts over with split bf16
+  // weights (two products per weight).  Waves that never read such a tile
+  // do not depend on it, so a finite fp16 pass is exact to its own rounding.
   bool done = false;
-  if constexpr (std::is_same<T, BF16>::value) done = run(std::true_type{});
+  if constexpr (std::is_same<T, BF16>::value) {
+    run(std::true_type{});
+    bool bad = false;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(o[dt][i]);
+    done = !__syncthreads_or(bad);
+  }
   if (!done) {
     m_run = -INFINITY;
     l_run = 0.f;
