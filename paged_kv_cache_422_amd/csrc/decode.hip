@@ -587,17 +587,26 @@ void decode_partition_kernel(DecodeArgs a) {
 // The whole block table of the sequence sits in registers (at most 64 *
 // kBtRegs blocks) and at most PMAX partitions fit in LDS; the host only picks
 // this kernel when both hold.
+//
+// Two groups of 4 waves (short partitions) keep one block in flight in two
+// buffers and are capped at 3 waves per SIMD (144 registers), and their LDS
+// budget is 78 KB whenever that still holds 8 partitions (a 4096-token
+// context in 512-token partitions), so two workgroups fit a CU and one can
+// start while the other ends.  Measured on MI355X, same box, three
+// alternating runs, the 8B-GQA batch at 512-token partitions: 404.1-405.7 ->
+// 399.4-400.0 us (two buffers and the cap alone: 403.1-403.5).  The 8-wave
+// form (partitions of 2048 tokens and up) needs 2 waves per SIMD per
+// workgroup, so a second one never fits; it keeps three buffers and 150 KB.
 template <int VW, int NH, int D, int THREADS>
 constexpr int fused_max_parts() {
-  // LDS budget per workgroup: two 256-thread workgroups or one 512-thread
-  // workgroup per CU (160 KB).
-  constexpr int budget = THREADS <= 256 ? 78 * 1024 : 150 * 1024;
   constexpr int per_part = (VW * NH * (D + 2) + 2 * NH) * 4;
+  constexpr int small = 78 * 1024;
+  constexpr int budget = (THREADS <= 256 || (VW == 4 && small / per_part >= 8)) ? small : 150 * 1024;
   return budget / per_part < 32 ? budget / per_part : 32;
 }
 
 template <class T, int D, int NH, int W, int NGRP>
-__global__ __launch_bounds__(64 * W * NGRP) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * W * NGRP) __attribute__((amdgpu_waves_per_eu(2, W == 4 ? 3 : 2)))
 void decode_fused_kernel(DecodeArgs a) {
   constexpr int VW = W;
   constexpr int kThreads = 64 * W * NGRP;
@@ -649,7 +658,8 @@ void decode_fused_kernel(DecodeArgs a) {
   const uint16_t* kbase = a.k_cache + g * tile_elems + hl * 32 + 8 * quad;
   const uint16_t* vbase = a.v_cache + g * tile_elems + quad * (4 * D) + hl * 4;
   const SegmentWalk<VW, decltype(pstart)> walk{NGRP, np, wl, W, pstart};
-  run_wave<T, D, NH, PMAX * VW, VW, 3>(walk, gi, bt, 0, L, qb, a.scale_log2, kbase, vbase, blk_elems, lane, st);
+  run_wave<T, D, NH, PMAX * VW, VW, W == 4 ? 2 : 3>(walk, gi, bt, 0, L, qb, a.scale_log2, kbase, vbase, blk_elems,
+                                                   lane, st);
   __syncthreads();
 
   // Per partition, the VW wave states merged (same code as the two-pass
