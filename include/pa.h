@@ -50,6 +50,13 @@
  * kernels, and a sequence with an out-of-range block id or context length
  * gets NaN output rows.  No call reads or writes outside the buffers it is
  * given when the sizes passed to it are right.
+ *
+ * Cache slots past a sequence's length may hold anything, NaN included; they
+ * never reach a result.  Inf or NaN in a key or value a sequence does hold
+ * reaches the rows that attend to it, as in the definition; in chunked
+ * prefill an inf or NaN value can also reach the earlier rows of the chunk
+ * that share its 64-key tile (their weight for it is 0, and 0 * inf is NaN
+ * in the matrix product).
  */
 #ifndef PA_H
 #define PA_H
