@@ -54,9 +54,10 @@
  * Cache slots past a sequence's length may hold anything, NaN included; they
  * never reach a result.  Inf or NaN in a key or value a sequence does hold
  * reaches the rows that attend to it, as in the definition; in chunked
- * prefill an inf or NaN value can also reach the earlier rows of the chunk
- * that share its 64-key tile (their weight for it is 0, and 0 * inf is NaN
- * in the matrix product).
+ * prefill an inf or NaN value can also reach some of the (at most 95) rows
+ * just before the first row that attends to it, those computed with its
+ * 64-key tile in the same 32-row group (their weight for it is 0, and
+ * 0 * inf is NaN in the matrix product).
  */
 #ifndef PA_H
 #define PA_H
