@@ -57,6 +57,8 @@ def test_decode_plan_reports_the_merge_path():
         ((128, 128, 8, 128, 4096, 512), (512, pa.MERGE_TWO_PASS, 4)),   # 16-head groups: two passes
         ((1024, 8, 8, 128, 8192, 4096), (4096, pa.MERGE_TWO_PASS, 8)),  # contexts beyond 4096 tokens
         ((256, 32, 8, 128, 4096, 16), (16, pa.MERGE_TWO_PASS, 4)),      # 256 partitions: beyond LDS
+        ((256, 32, 8, 128, 4096, 256), (256, pa.MERGE_TWO_PASS, 4)),    # 16 partitions: beyond the 78 KB form
+        ((128, 64, 8, 128, 4096, 512), (512, pa.MERGE_ON_CHIP, 4)),     # 8-head groups keep 150 KB: 8 fit
     ]
     for args, want in cases:
         assert pa.decode_plan(*args) == want, args

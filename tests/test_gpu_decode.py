@@ -146,14 +146,17 @@ def test_batch_invariance_is_bit_exact():
 # two-pass kernels (partition states through the workspace).  Both must give
 # the same bits.  Cases: bf16 GQA at the 8B workload's 512-token partitions
 # (4-wave groups), fp16 MHA at 256-token partitions, bf16 GQA at 2048-token
-# partitions (8-wave groups), head_dim 64 with 8- and 2-head groups.
+# partitions (8-wave groups), head_dim 64 with 8- and 2-head groups, and
+# 8-head groups at head_dim 128 (the form that keeps the larger LDS budget).
 @pytest.mark.parametrize("dtype,S,Hq,Hkv,D,P,max_len", [
     (torch.bfloat16, 128, 32, 8, 128, 512, 4096),
     (torch.float16, 32, 32, 32, 128, 256, 2048),
     (torch.bfloat16, 128, 32, 8, 128, 2048, 4096),
     (torch.float16, 128, 64, 8, 64, 1024, 4096),
     (torch.bfloat16, 64, 32, 16, 64, 256, 1024),
-], ids=["bf16-gqa4-P512", "fp16-mha-P256", "bf16-gqa4-P2048", "fp16-gqa8-D64-P1024", "bf16-gqa2-D64-P256"])
+    (torch.bfloat16, 128, 64, 8, 128, 512, 4096),
+], ids=["bf16-gqa4-P512", "fp16-mha-P256", "bf16-gqa4-P2048", "fp16-gqa8-D64-P1024", "bf16-gqa2-D64-P256",
+        "bf16-gqa8-P512"])
 def test_single_pass_merge_matches_two_pass_bits(dtype, S, Hq, Hkv, D, P, max_len):
     rng = np.random.default_rng(21)
     lens = rng.integers(1, max_len + 1, S)
