@@ -83,6 +83,9 @@ def parse():
                     help="do not evict the Infinity Cache between steps")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured into a HIP graph and replayed")
+    ap.add_argument("--overlap", action="store_true",
+                    help="mixed step: also time it with the prefill chunks on a second stream, "
+                         "concurrent with the decode")
     ap.add_argument("--settle", type=float, default=5.0,
                     help="seconds to wait before building the workload, so that memory an earlier process "
                          "freed on the GPU has been reclaimed (0: no wait)")
@@ -804,6 +807,28 @@ def main():
             "contiguous_blocks_GBps": round(gbs_c, 1), "frac_of_contiguous": round(gbs / gbs_c, 4),
             "reference": "2 GiB device-to-device copy (read + write bytes); the same decode with each "
                          "sequence's blocks consecutive in memory, same run"}
+
+    if args.overlap and name == "mixed":
+        # The prefill chunks and the decode only read the cache once the
+        # write is done, so a caller can run them concurrently: the prefill on
+        # a second stream (default priority) that waits for the write, the
+        # decode on this one, and this stream waits for the second at the end.
+        side = torch.cuda.Stream()
+        written = torch.cuda.Event()
+
+        def step_two_streams():
+            fns[0]()
+            written.record()
+            side.wait_event(written)
+            with torch.cuda.stream(side):
+                fns[1]()
+            fns[2]()
+            torch.cuda.current_stream().wait_stream(side)
+
+        timer.run(args.warmup, [step_two_streams])
+        _, tot_o, wall_o = timer.run(args.steps, [step_two_streams])
+        extra["two_streams"] = {"us_per_step": round(mean(tot_o) * 1e3, 2), "wall_ms_per_step": round(wall_o, 5),
+                                "one_stream_us_per_step": round(ms * 1e3, 2)}
 
     if args.graph:
         # The same calls captured once into a HIP graph; each step replays it.
