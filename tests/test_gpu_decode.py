@@ -61,7 +61,8 @@ def test_tiny_workload():
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (8, 2, 128), (32, 8, 128), (16, 1, 64),
-                                      (40, 40, 128), (32, 1, 128), (6, 2, 64), (16, 8, 128), (64, 8, 64)])
+                                      (40, 40, 128), (32, 1, 128), (6, 2, 64), (16, 8, 128), (64, 8, 64),
+                                      (24, 1, 128), (48, 4, 64)])
 @pytest.mark.parametrize("P", [0, 16, 256])
 def test_decode_shapes(dtype, Hq, Hkv, D, P):
     lens = [1, 15, 16, 17, 100, 511, 512, 513, 1030]

@@ -67,8 +67,9 @@ def test_prefill_shapes(dtype, Hq, Hkv, D):
 
 @pytest.mark.parametrize("Hq,Hkv,D,dtype", [(4, 2, 128, torch.bfloat16), (16, 8, 64, torch.float16),
                                             (16, 2, 128, torch.float16), (32, 2, 64, torch.bfloat16),
-                                            (32, 1, 128, torch.bfloat16)],
-                         ids=["g2", "g2-D64", "g8", "g16-D64", "g32"])
+                                            (32, 1, 128, torch.bfloat16), (24, 1, 128, torch.float16),
+                                            (12, 4, 64, torch.bfloat16)],
+                         ids=["g2", "g2-D64", "g8", "g16-D64", "g32", "g24", "g3-D64"])
 def test_prefill_group_sizes(Hq, Hkv, D, dtype):
     """Query-head groups of 2, 8, 16 and 32 per KV head: a workgroup then
     covers 2 heads x 4 row tiles or 4 heads x 2 row tiles, and a KV group
