@@ -666,7 +666,7 @@ def bench_beam(args, np, torch, pa):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by sequence or KV head with no exchange inside attention, "
               "but runs on more than one GPU are not part of it.", file=sys.stderr)
         return 2
